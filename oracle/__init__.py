@@ -1,0 +1,15 @@
+"""Oracle for pair-biased (gated) triangle self-attention -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, float64 CPU implementations that the HIP library is checked
+against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` may import anything from here; the library itself never
+does, and this package imports nothing from the library.
+
+* ``oracle.ref``   -- vectorised NumPy float64, materialises the full softmax.
+* ``oracle.brute`` -- pure-Python scalar loops for tiny inputs.
+
+Parity status: every function here is pinned by ``tests/test_oracle.py``
+(brute force, torch CPU library routines, closed forms, invariants, and a
+hand-derived golden case under ``tests/golden/``).  No function is
+"parity unpinned".
+"""
