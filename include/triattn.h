@@ -1,0 +1,177 @@
+/*
+ * triattn.h -- C ABI of libtriattn.so: pair-biased (gated) triangle self-attention
+ * over the pair representation Z (I x I x c_z) on AMD Instinct MI355X (gfx950).
+ *
+ * The operator.  The pair representation is an I x I array of c_z-vectors
+ * ("tokens"), c_z = 128 (LightNobel article, section 1.1).  Triangular attention
+ * is the pair-tensor operator the LightNobel article singles out in section 3.1;
+ * the pages never print its equations, and this library computes the standard
+ * gated form (eps 1e-5, biased variance, softmax scale 1/sqrt(d)):
+ *
+ *   x_ij   = LayerNorm(z_ij) * gamma + beta
+ *   q,k,v  = x W_q^T, x W_k^T, x W_v^T          split into H heads of width d
+ *   b_jk^h = x_jk . W_b[h]                       pair bias, one scalar per head
+ *   g_ij   = sigmoid(x_ij W_g^T + b_g)
+ *   start: o_ij^h = sum_k softmax_k(q_ij^h.k_ik^h/sqrt(d) + b_jk^h) v_ik^h
+ *   end:   o_ij^h = sum_k softmax_k(q_ij^h.k_kj^h/sqrt(d) + b_ki^h) v_kj^h
+ *   out_ij = (g_ij * o_ij) W_o^T + b_o
+ *
+ * The softmax over keys is evaluated blockwise with a running maximum and sum,
+ * so no I x I score matrix is ever stored (the on-the-fly scoring of ring
+ * attention, Design-CP summary, Methodology section 1).  The row-block entry
+ * point is one device's share under 1D row sharding (Design-CP summary,
+ * Methodology section 1): a block of query rows with its own keys and values
+ * and the whole pair bias held locally.
+ *
+ * Conventions shared by every entry point
+ *  - All pointers are DEVICE pointers unless stated, 16-byte aligned, dense
+ *    row-major (C order).  "cdt" = the compute dtype of the problem
+ *    (TA_BF16: bfloat16, TA_F32: float32).
+ *  - Weights follow torch.nn.Linear: W[out][in], y = x W^T.
+ *  - The caller owns every buffer (inputs, weights, outputs, workspace).
+ *    The library never allocates, frees or synchronises; it only enqueues
+ *    kernels on `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *  - Every argument is validated on the host before anything is enqueued; on
+ *    error nothing is launched and no output is touched.  Execution errors of
+ *    an enqueued kernel surface at the caller's next synchronisation.
+ *  - No global mutable state: calls are thread-safe; calls that share a
+ *    workspace must be ordered by the caller (same stream or events).
+ *  - Supported shapes: c_z = 128, heads * head_dim = 128, head_dim = 32, any
+ *    I >= 1 (ragged tails handled), 1 <= rows <= I.  I * I * max(c_z, ...) must
+ *    fit the 32-bit element offsets used internally: I <= 16384.
+ */
+#ifndef TRIATTN_H
+#define TRIATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TRIATTN_ABI_VERSION 1
+
+/* Compute dtypes. */
+enum { TA_BF16 = 1, TA_F32 = 2 };
+
+/* Variants (workspace sizing, stage entry points). */
+enum { TA_START = 0, TA_END = 1, TA_ROWS = 2 };
+
+/* Return codes: 0 = success, negative = error (nothing was enqueued). */
+enum {
+  TA_OK = 0,
+  TA_ERR_NULL_PTR = -1,          /* a required pointer is NULL */
+  TA_ERR_BAD_SHAPE = -2,         /* I < 1, rows < 1, rows > I (or != I for start/end), I too large, row0 out of range */
+  TA_ERR_UNSUPPORTED = -3,       /* c_z, heads, head_dim other than 128, 4, 32 */
+  TA_ERR_BAD_DTYPE = -4,         /* dtype not TA_BF16 / TA_F32 */
+  TA_ERR_WORKSPACE_TOO_SMALL = -5,
+  TA_ERR_MISALIGNED = -6,        /* a pointer is not 16-byte aligned */
+  TA_ERR_ALIAS = -7,             /* out overlaps an input or the workspace (out == z is allowed) */
+  TA_ERR_HIP = -8,               /* a kernel launch was rejected by the HIP runtime */
+  TA_ERR_BAD_VARIANT = -9,
+  TA_ERR_BAD_EPS = -10           /* ln_eps not finite and > 0 */
+};
+
+/* Problem description (host memory). */
+typedef struct ta_problem {
+  int32_t I;         /* side of the pair tensor: keys per attention row */
+  int32_t rows;      /* query rows computed: I for start/end; 1..I for the row block */
+  int32_t c_z;       /* channels per token (128) */
+  int32_t heads;     /* H (4) */
+  int32_t head_dim;  /* d (32) */
+  int32_t dtype;     /* TA_BF16 or TA_F32 */
+  float ln_eps;      /* LayerNorm epsilon, e.g. 1e-5 */
+} ta_problem;
+
+/* Weights of one triangle-attention block (host struct of device pointers). */
+typedef struct ta_weights {
+  const float* ln_gamma; /* fp32 [c_z] LayerNorm scale (required) */
+  const float* ln_beta;  /* fp32 [c_z] LayerNorm shift (required) */
+  const void* w_q;       /* cdt [H*d][c_z] */
+  const void* w_k;       /* cdt [H*d][c_z] */
+  const void* w_v;       /* cdt [H*d][c_z] */
+  const void* w_g;       /* cdt [H*d][c_z] gate projection */
+  const void* w_b;       /* cdt [H][c_z]   pair-bias projection */
+  const float* b_g;      /* fp32 [H*d] gate bias, or NULL for zero */
+  const void* w_o;       /* cdt [c_z][H*d] output projection */
+  const float* b_o;      /* fp32 [c_z] output bias, or NULL for zero */
+} ta_weights;
+
+/* Byte offsets of the intermediates inside a workspace, and their layouts.
+ * L = lines (rows of Z for start/rows, columns of Z for end), P = positions
+ * padded to a multiple of 128 (padding holds finite values).
+ *   q    cdt  [L][H][P][d]   query, already multiplied by 1/sqrt(d)
+ *   k    cdt  [L][H][P][d]
+ *   vt   cdt  [L][H][d][P]   value, transposed per head
+ *   g    cdt  [L][H][P][d]   gate after the sigmoid
+ *   bias fp32 [H][I][I]      start/end only (absent for the row block);
+ *                            end stores the transposed bias b_ki at [h][i][k]
+ * For the end variant line = column j of Z and position = row i.           */
+typedef struct ta_ws_layout {
+  size_t q, k, vt, g, bias; /* byte offsets; bias = (size_t)-1 when absent */
+  size_t total;             /* bytes required */
+  int32_t lines, positions; /* L and padded P */
+} ta_ws_layout;
+
+/* ABI version of the loaded library (TRIATTN_ABI_VERSION). */
+int triangle_attn_abi_version(void);
+
+/* Static description of an error code. */
+const char* triangle_attn_strerror(int code);
+
+/* Workspace size and layout for `variant` (TA_START, TA_END, TA_ROWS).
+ * Host-only; never touches the device.  Returns TA_OK or a validation error. */
+int triangle_attn_workspace_layout(const ta_problem* prob, int variant, ta_ws_layout* layout);
+
+/* Starting-node triangle attention (equations above).
+ *   z   cdt [I][I][c_z]  input pair tensor
+ *   out cdt [I][I][c_z]  result (the update only: z is not added); out == z is allowed
+ *   ws  workspace of at least triangle_attn_workspace_layout(TA_START).total bytes
+ * Requires prob->rows == prob->I. */
+int triangle_attn_start(const ta_problem* prob, const ta_weights* w, const void* z, void* out,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Ending-node triangle attention: attention runs down the columns of Z with
+ * bias b_ki.  Same arguments as triangle_attn_start; end(Z) equals
+ * start(Z^T)^T for the same weights. */
+int triangle_attn_end(const ta_problem* prob, const ta_weights* w, const void* z, void* out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Row block (one device's share under 1D row sharding).
+ *   prob->I     full side (keys per row), prob->rows = R query rows
+ *   z_rows cdt  [R][I][c_z]   R consecutive rows of Z
+ *   bias   fp32 [H][I][I]     the whole pair bias, bias[h][j][k] = b_jk^h (e.g. built
+ *                             with triangle_attn_pair_bias); rows are independent,
+ *                             so the global offset of the block is not needed
+ *   out    cdt  [R][I][c_z]
+ *   ws     at least triangle_attn_workspace_layout(TA_ROWS).total bytes */
+int triangle_attn_start_rows(const ta_problem* prob, const ta_weights* w, const void* z_rows,
+                             const float* bias, void* out, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Pair bias of a block of rows: bias[h][row0 + r][k] = b^h(z_rows[r][k]) for
+ * r < prob->rows, written into a whole [H][I][I] fp32 array (other rows are
+ * untouched).  Uses the same kernel and accumulation order as the bias
+ * computed inside triangle_attn_start, so the two agree bit for bit.
+ * Requires 0 <= row0 and row0 + rows <= I. */
+int triangle_attn_pair_bias(const ta_problem* prob, const ta_weights* w, const void* z_rows,
+                            int32_t row0, float* bias, void* stream);
+
+/* Stage 1 alone: LayerNorm + projections of `variant` into the workspace
+ * (layout above).  z is [I][I][c_z] for start/end, [R][I][c_z] for rows. */
+int triangle_attn_project(const ta_problem* prob, int variant, const ta_weights* w,
+                          const void* z, void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 2 alone: fused attention + gate + output projection from a workspace
+ * filled by triangle_attn_project with the same problem and variant.  `bias`
+ * is required for TA_ROWS and must be NULL otherwise (the workspace holds it). */
+int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* w,
+                         const float* bias, void* out, const void* ws, size_t ws_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRIATTN_H */

@@ -160,3 +160,20 @@ def params(weights_f64: dict, heads: int, head_dim: int, eps: float = 1e-5) -> d
     p.update(heads=heads, head_dim=head_dim, eps=eps)
     return p
 
+
+
+def triangle_attn_rows_queries(z_rows, bias_q, queries, p):
+    """Row-block attention evaluated only at some query positions.
+
+    For every line r of z_rows [R][I][c_z] and every n, the output token of
+    query position queries[n]; bias_q[h][n][k] is the bias of that query
+    against key k.  Same definition as triangle_attn_rows, restricted to the
+    chosen queries (large problems are checked on such samples).
+    """
+    queries = np.asarray(queries)
+    out = []
+    for zi in z_rows:
+        q, k, v, g, _ = project(zi, p)
+        o = attend(q[queries], k, v, bias_q, p["head_dim"])
+        out.append(gate_and_project_out(o, g[queries], p))
+    return np.stack(out)

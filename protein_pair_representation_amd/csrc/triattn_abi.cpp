@@ -1,0 +1,280 @@
+// triattn_abi.cpp -- the C ABI of libtriattn.so (declared in include/triattn.h).
+//
+// Host-side only: validates every argument, sizes the workspace, and enqueues
+// the two kernels on the caller's stream.  Nothing here allocates, frees or
+// synchronises, and no HIP call is made before validation has passed.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/triattn.h"
+#include "triattn_kernels.h"
+
+namespace {
+
+constexpr int kCz = 128, kHeads = 4, kHeadDim = 32, kPosAlign = 128, kMaxI = 65536;
+
+size_t esize(int dtype) { return dtype == TA_BF16 ? 2 : 4; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Span {
+  const void* p;
+  size_t n;
+};
+bool overlap(Span a, Span b) {
+  if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
+  uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+int check_problem(const ta_problem* p, int variant) {
+  if (p == nullptr) return TA_ERR_NULL_PTR;
+  if (variant != TA_START && variant != TA_END && variant != TA_ROWS) return TA_ERR_BAD_VARIANT;
+  if (p->dtype != TA_BF16 && p->dtype != TA_F32) return TA_ERR_BAD_DTYPE;
+  if (p->c_z != kCz || p->heads != kHeads || p->head_dim != kHeadDim) return TA_ERR_UNSUPPORTED;
+  if (p->I < 1 || p->I > kMaxI || p->rows < 1 || p->rows > p->I) return TA_ERR_BAD_SHAPE;
+  if (variant != TA_ROWS && p->rows != p->I) return TA_ERR_BAD_SHAPE;
+  if (!(p->ln_eps > 0.0f) || !isfinite(p->ln_eps)) return TA_ERR_BAD_EPS;
+  return TA_OK;
+}
+
+void layout_of(const ta_problem* p, int variant, ta_ws_layout* l) {
+  const size_t lines = (size_t)(variant == TA_ROWS ? p->rows : p->I);
+  const size_t P = ((size_t)p->I + kPosAlign - 1) / kPosAlign * kPosAlign;
+  const size_t region = align256(lines * kHeads * P * kHeadDim * esize(p->dtype));
+  l->lines = (int32_t)lines;
+  l->positions = (int32_t)P;
+  l->q = 0;
+  l->k = region;
+  l->vt = 2 * region;
+  l->g = 3 * region;
+  size_t total = 4 * region;
+  if (variant == TA_ROWS) {
+    l->bias = (size_t)-1;
+  } else {
+    l->bias = total;
+    total += align256((size_t)kHeads * p->I * p->I * sizeof(float));
+  }
+  l->total = total;
+}
+
+int check_weights(const ta_weights* w) {
+  if (w == nullptr) return TA_ERR_NULL_PTR;
+  const void* req[] = {w->ln_gamma, w->ln_beta, w->w_q, w->w_k, w->w_v, w->w_g, w->w_b, w->w_o};
+  for (const void* q : req)
+    if (q == nullptr) return TA_ERR_NULL_PTR;
+  const void* all[] = {w->ln_gamma, w->ln_beta, w->w_q, w->w_k, w->w_v, w->w_g, w->w_b, w->w_o, w->b_g, w->b_o};
+  for (const void* q : all)
+    if (q != nullptr && !aligned16(q)) return TA_ERR_MISALIGNED;
+  return TA_OK;
+}
+
+// Out must not overlap any input, weight or the workspace (out == z exactly is fine).
+int check_out_alias(const ta_problem* p, const ta_weights* w, Span out, Span z, Span ws, Span bias) {
+  const size_t es = esize(p->dtype);
+  const Span wspans[] = {{w->ln_gamma, kCz * 4}, {w->ln_beta, kCz * 4}, {w->w_q, (size_t)kCz * kCz * es},
+                         {w->w_k, (size_t)kCz * kCz * es}, {w->w_v, (size_t)kCz * kCz * es},
+                         {w->w_g, (size_t)kCz * kCz * es}, {w->w_b, (size_t)kHeads * kCz * es},
+                         {w->b_g, kCz * 4}, {w->w_o, (size_t)kCz * kCz * es}, {w->b_o, kCz * 4}};
+  for (const Span& s : wspans) {
+    if (overlap(out, s) || overlap(ws, s)) return TA_ERR_ALIAS;
+  }
+  if (overlap(out, ws) || overlap(out, bias) || overlap(ws, z) || overlap(ws, bias)) return TA_ERR_ALIAS;
+  if (out.p != z.p && overlap(out, z)) return TA_ERR_ALIAS;
+  return TA_OK;
+}
+
+triattn::ProjectArgs project_args(const ta_problem* p, int variant, const ta_weights* w, const void* z,
+                                  void* ws, const ta_ws_layout& l) {
+  triattn::ProjectArgs a;
+  memset(&a, 0, sizeof(a));
+  a.z = z;
+  if (variant == TA_END) {  // line = column j, position = row i
+    a.z_line_stride = kCz;
+    a.z_pos_stride = (int64_t)p->I * kCz;
+  } else {
+    a.z_line_stride = (int64_t)p->I * kCz;
+    a.z_pos_stride = kCz;
+  }
+  a.ln_gamma = w->ln_gamma;
+  a.ln_beta = w->ln_beta;
+  a.eps = p->ln_eps;
+  a.w_q = w->w_q;
+  a.w_k = w->w_k;
+  a.w_v = w->w_v;
+  a.w_g = w->w_g;
+  a.w_b = w->w_b;
+  a.b_g = w->b_g;
+  char* base = (char*)ws;
+  a.q = base + l.q;
+  a.k = base + l.k;
+  a.vt = base + l.vt;
+  a.g = base + l.g;
+  a.bias = variant == TA_ROWS ? nullptr : (float*)(base + l.bias);
+  a.bias_row0 = 0;
+  a.I = p->I;
+  a.P = l.positions;
+  a.lines = l.lines;
+  a.bias_only = 0;
+  return a;
+}
+
+triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weights* w, const float* bias,
+                                void* out, const void* ws, const ta_ws_layout& l) {
+  triattn::AttendArgs a;
+  memset(&a, 0, sizeof(a));
+  const char* base = (const char*)ws;
+  a.q = base + l.q;
+  a.k = base + l.k;
+  a.vt = base + l.vt;
+  a.g = base + l.g;
+  a.bias = variant == TA_ROWS ? bias : (const float*)(base + l.bias);
+  a.w_o = w->w_o;
+  a.b_o = w->b_o;
+  a.out = out;
+  a.I = p->I;
+  a.P = l.positions;
+  a.lines = l.lines;
+  a.nqb = l.positions / kPosAlign;
+  a.out_transposed = variant == TA_END ? 1 : 0;
+  return a;
+}
+
+int enqueue(hipError_t e) { return e == hipSuccess ? TA_OK : TA_ERR_HIP; }
+
+// Shared driver of start / end / rows.
+int run_full(const ta_problem* p, int variant, const ta_weights* w, const void* z, const float* bias,
+             void* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_problem(p, variant);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (z == nullptr || out == nullptr || ws == nullptr) return TA_ERR_NULL_PTR;
+  if (variant == TA_ROWS && bias == nullptr) return TA_ERR_NULL_PTR;
+  if (!aligned16(z) || !aligned16(out) || !aligned16(ws) || (bias && !aligned16(bias))) return TA_ERR_MISALIGNED;
+  ta_ws_layout l;
+  layout_of(p, variant, &l);
+  if (ws_bytes < l.total) return TA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t tok_bytes = (size_t)p->rows * p->I * kCz * esize(p->dtype);
+  const Span bspan = {bias, bias ? (size_t)kHeads * p->I * p->I * sizeof(float) : 0};
+  if ((rc = check_out_alias(p, w, {out, tok_bytes}, {z, tok_bytes}, {ws, l.total}, bspan))) return rc;
+
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();  // clear a stale error so that only our launches are reported
+  triattn::ProjectArgs pa = project_args(p, variant, w, z, ws, l);
+  if ((rc = enqueue(triattn::launch_project(pa, p->dtype, s)))) return rc;
+  triattn::AttendArgs aa = attend_args(p, variant, w, bias, out, ws, l);
+  return enqueue(triattn::launch_attend(aa, p->dtype, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int triangle_attn_abi_version(void) { return TRIATTN_ABI_VERSION; }
+
+const char* triangle_attn_strerror(int code) {
+  switch (code) {
+    case TA_OK: return "success";
+    case TA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case TA_ERR_BAD_SHAPE: return "bad shape (I, rows or row0 out of range)";
+    case TA_ERR_UNSUPPORTED: return "unsupported c_z / heads / head_dim (need 128 / 4 / 32)";
+    case TA_ERR_BAD_DTYPE: return "dtype must be TA_BF16 or TA_F32";
+    case TA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case TA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case TA_ERR_ALIAS: return "output overlaps an input, a weight or the workspace";
+    case TA_ERR_HIP: return "HIP runtime rejected a kernel launch";
+    case TA_ERR_BAD_VARIANT: return "unknown variant";
+    case TA_ERR_BAD_EPS: return "ln_eps must be finite and positive";
+    default: return "unknown error code";
+  }
+}
+
+int triangle_attn_workspace_layout(const ta_problem* prob, int variant, ta_ws_layout* layout) {
+  int rc = check_problem(prob, variant);
+  if (rc) return rc;
+  if (layout == nullptr) return TA_ERR_NULL_PTR;
+  layout_of(prob, variant, layout);
+  return TA_OK;
+}
+
+int triangle_attn_start(const ta_problem* prob, const ta_weights* w, const void* z, void* out, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return run_full(prob, TA_START, w, z, nullptr, out, ws, ws_bytes, stream);
+}
+
+int triangle_attn_end(const ta_problem* prob, const ta_weights* w, const void* z, void* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return run_full(prob, TA_END, w, z, nullptr, out, ws, ws_bytes, stream);
+}
+
+int triangle_attn_start_rows(const ta_problem* prob, const ta_weights* w, const void* z_rows, const float* bias,
+                             void* out, void* ws, size_t ws_bytes, void* stream) {
+  return run_full(prob, TA_ROWS, w, z_rows, bias, out, ws, ws_bytes, stream);
+}
+
+int triangle_attn_pair_bias(const ta_problem* prob, const ta_weights* w, const void* z_rows, int32_t row0,
+                            float* bias, void* stream) {
+  int rc = check_problem(prob, TA_ROWS);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (z_rows == nullptr || bias == nullptr) return TA_ERR_NULL_PTR;
+  if (row0 < 0 || (int64_t)row0 + prob->rows > prob->I) return TA_ERR_BAD_SHAPE;
+  if (!aligned16(z_rows) || !aligned16(bias)) return TA_ERR_MISALIGNED;
+  const size_t bias_bytes = (size_t)kHeads * prob->I * prob->I * sizeof(float);
+  const size_t tok_bytes = (size_t)prob->rows * prob->I * kCz * esize(prob->dtype);
+  if ((rc = check_out_alias(prob, w, {bias, bias_bytes}, {z_rows, tok_bytes}, {nullptr, 0}, {nullptr, 0})))
+    return rc;
+  if (overlap({bias, bias_bytes}, {z_rows, tok_bytes})) return TA_ERR_ALIAS;
+  ta_ws_layout l;
+  layout_of(prob, TA_ROWS, &l);
+  triattn::ProjectArgs a = project_args(prob, TA_ROWS, w, z_rows, nullptr, l);
+  a.q = a.k = a.vt = a.g = nullptr;
+  a.bias = bias;
+  a.bias_row0 = row0;
+  a.bias_only = 1;
+  (void)hipGetLastError();
+  return enqueue(triattn::launch_project(a, prob->dtype, (hipStream_t)stream));
+}
+
+int triangle_attn_project(const ta_problem* prob, int variant, const ta_weights* w, const void* z, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int rc = check_problem(prob, variant);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (z == nullptr || ws == nullptr) return TA_ERR_NULL_PTR;
+  if (!aligned16(z) || !aligned16(ws)) return TA_ERR_MISALIGNED;
+  ta_ws_layout l;
+  layout_of(prob, variant, &l);
+  if (ws_bytes < l.total) return TA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t tok_bytes = (size_t)prob->rows * prob->I * kCz * esize(prob->dtype);
+  if ((rc = check_out_alias(prob, w, {ws, l.total}, {z, tok_bytes}, {nullptr, 0}, {nullptr, 0}))) return rc;
+  if (overlap({ws, l.total}, {z, tok_bytes})) return TA_ERR_ALIAS;
+  (void)hipGetLastError();
+  triattn::ProjectArgs a = project_args(prob, variant, w, z, ws, l);
+  return enqueue(triattn::launch_project(a, prob->dtype, (hipStream_t)stream));
+}
+
+int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* w, const float* bias, void* out,
+                         const void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_problem(prob, variant);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (out == nullptr || ws == nullptr) return TA_ERR_NULL_PTR;
+  if (variant == TA_ROWS && bias == nullptr) return TA_ERR_NULL_PTR;
+  if (variant != TA_ROWS && bias != nullptr) return TA_ERR_BAD_VARIANT;
+  if (!aligned16(out) || !aligned16(ws) || (bias && !aligned16(bias))) return TA_ERR_MISALIGNED;
+  ta_ws_layout l;
+  layout_of(prob, variant, &l);
+  if (ws_bytes < l.total) return TA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t tok_bytes = (size_t)prob->rows * prob->I * kCz * esize(prob->dtype);
+  const Span bspan = {bias, bias ? (size_t)kHeads * prob->I * prob->I * sizeof(float) : 0};
+  if ((rc = check_out_alias(prob, w, {out, tok_bytes}, {nullptr, 0}, {ws, l.total}, bspan))) return rc;
+  (void)hipGetLastError();
+  triattn::AttendArgs a = attend_args(prob, variant, w, bias, out, ws, l);
+  return enqueue(triattn::launch_attend(a, prob->dtype, (hipStream_t)stream));
+}
+
+}  // extern "C"

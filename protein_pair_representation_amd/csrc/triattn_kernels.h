@@ -1,0 +1,39 @@
+// Internal interface between the C ABI layer and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace triattn {
+
+// K1: LayerNorm + projections of `lines` x `P` tokens (positions >= I are padding).
+// Token (line, pos) is read at z + line * z_line_stride + pos * z_pos_stride (elements).
+struct ProjectArgs {
+  const void* z;
+  int64_t z_line_stride, z_pos_stride;
+  const float* ln_gamma;
+  const float* ln_beta;
+  float eps;
+  const void *w_q, *w_k, *w_v, *w_g, *w_b;
+  const float* b_g;
+  void *q, *k, *vt, *g;   // workspace regions (unused when bias_only)
+  float* bias;            // [H][I][I] or nullptr
+  int bias_row0;          // bias row of line 0
+  int I, P, lines;
+  int bias_only;
+};
+
+// K2: fused attention over `lines` lines of `I` keys, queries in blocks of 128.
+struct AttendArgs {
+  const void *q, *k, *vt, *g;
+  const float* bias;      // [H][I][I]
+  const void* w_o;
+  const float* b_o;       // or nullptr
+  void* out;
+  int I, P, lines, nqb;
+  int out_transposed;     // 1: out[j][line], 0: out[line][j]
+};
+
+hipError_t launch_project(const ProjectArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_attend(const AttendArgs& a, int dtype, hipStream_t stream);
+
+}  // namespace triattn

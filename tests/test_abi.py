@@ -1,0 +1,174 @@
+"""The C ABI on the host: the library loads, exports what the header declares,
+and rejects every bad argument before anything touches the device.
+
+Pointers here are fake device addresses: every case fails validation, which
+never dereferences a pointer and makes no HIP call, so this runs without a GPU.
+"""
+import ctypes
+
+import pytest
+
+from protein_pair_representation_amd import triattn as ta
+
+A = 0x7F0000000000  # a 256-byte aligned fake device address
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ta.load_library()
+
+
+def prob(I=64, rows=None, dtype=ta.TA_BF16, c_z=128, heads=4, hd=32, eps=1e-5):
+    return ta.TaProblem(I, I if rows is None else rows, c_z, heads, hd, dtype, eps)
+
+
+def weights(base=A + 900 * MB, **over):
+    w = ta.TaWeights()
+    for n_, name in enumerate(ta._WEIGHT_FIELDS):
+        setattr(w, name, base + n_ * MB)
+    for k, v in over.items():
+        setattr(w, k, v)
+    return w
+
+
+def layout(lib, p, variant):
+    lay = ta.TaWsLayout()
+    rc = lib.triangle_attn_workspace_layout(ctypes.byref(p), variant, ctypes.byref(lay))
+    return rc, lay
+
+
+def test_exports_match_header(lib):
+    names = ta.header_functions()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror(lib):
+    assert lib.triangle_attn_abi_version() == 1
+    for code in range(0, -11, -1):
+        msg = lib.triangle_attn_strerror(code).decode()
+        assert msg and msg != "unknown error code"
+    assert lib.triangle_attn_strerror(-99).decode() == "unknown error code"
+
+
+@pytest.mark.parametrize("p,variant,code", [
+    (None, ta.TA_START, -1),
+    (prob(dtype=3), ta.TA_START, -4),
+    (prob(c_z=64), ta.TA_START, -3),
+    (prob(heads=8), ta.TA_START, -3),
+    (prob(hd=16), ta.TA_START, -3),
+    (prob(I=0), ta.TA_START, -2),
+    (prob(I=70000), ta.TA_START, -2),
+    (prob(I=64, rows=32), ta.TA_START, -2),
+    (prob(I=64, rows=32), ta.TA_END, -2),
+    (prob(I=64, rows=65), ta.TA_ROWS, -2),
+    (prob(I=64, rows=0), ta.TA_ROWS, -2),
+    (prob(eps=0.0), ta.TA_START, -10),
+    (prob(eps=float("nan")), ta.TA_START, -10),
+    (prob(), 7, -9),
+])
+def test_layout_rejects(lib, p, variant, code):
+    lay = ta.TaWsLayout()
+    rc = lib.triangle_attn_workspace_layout(None if p is None else ctypes.byref(p), variant, ctypes.byref(lay))
+    assert rc == code
+
+
+@pytest.mark.parametrize("I,rows,variant,dtype", [
+    (64, 64, ta.TA_START, ta.TA_F32), (384, 384, ta.TA_START, ta.TA_BF16), (1000, 1000, ta.TA_END, ta.TA_BF16),
+    (4096, 1024, ta.TA_ROWS, ta.TA_BF16), (5, 3, ta.TA_ROWS, ta.TA_F32), (1, 1, ta.TA_START, ta.TA_BF16)])
+def test_layout_sizes(lib, I, rows, variant, dtype):
+    rc, lay = layout(lib, prob(I, rows, dtype), variant)
+    assert rc == 0
+    es = 2 if dtype == ta.TA_BF16 else 4
+    P = (I + 127) // 128 * 128
+    region = lines = rows if variant == ta.TA_ROWS else I
+    region = (lines * 4 * P * 32 * es + 255) // 256 * 256
+    assert lay.lines == lines and lay.positions == P
+    assert (lay.q, lay.k, lay.vt, lay.g) == (0, region, 2 * region, 3 * region)
+    if variant == ta.TA_ROWS:
+        assert lay.bias == ctypes.c_size_t(-1).value and lay.total == 4 * region
+    else:
+        assert lay.bias == 4 * region
+        assert lay.total == 4 * region + (4 * I * I * 4 + 255) // 256 * 256
+
+
+def _start(lib, p=None, w="default", z=A, out=A + 100 * MB, ws=A + 200 * MB, ws_bytes=1 << 40, fn="start"):
+    p = prob() if p is None else p
+    w = weights() if w == "default" else w
+    f = getattr(lib, "triangle_attn_" + fn)
+    return f(ctypes.byref(p), None if w is None else ctypes.byref(w), z, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["start", "end"])
+def test_start_end_reject(lib, fn):
+    assert _start(lib, w=None, fn=fn) == -1
+    assert _start(lib, w=weights(w_q=None), fn=fn) == -1
+    assert _start(lib, w=weights(ln_gamma=None), fn=fn) == -1
+    assert _start(lib, z=None, fn=fn) == -1
+    assert _start(lib, out=None, fn=fn) == -1
+    assert _start(lib, ws=None, fn=fn) == -1
+    assert _start(lib, z=A + 8, fn=fn) == -6
+    assert _start(lib, out=A + 4, fn=fn) == -6
+    assert _start(lib, w=weights(w_o=A + 900 * MB + 8), fn=fn) == -6
+    assert _start(lib, w=weights(b_g=A + 900 * MB + 2), fn=fn) == -6
+    rc, lay = layout(lib, prob(), ta.TA_START)
+    assert _start(lib, ws_bytes=lay.total - 1, fn=fn) == -5
+    # out overlapping the workspace, or partially overlapping z
+    assert _start(lib, out=A + 200 * MB + 4096, fn=fn) == -7
+    assert _start(lib, out=A + 256, fn=fn) == -7
+    # out overlapping a weight
+    assert _start(lib, out=A + 900 * MB, fn=fn) == -7
+    # workspace overlapping z
+    assert _start(lib, ws=A + 1024, fn=fn) == -7
+    assert _start(lib, p=prob(dtype=0), fn=fn) == -4
+
+
+def test_rows_reject(lib):
+    p = prob(I=64, rows=16)
+    w = weights()
+    f = lib.triangle_attn_start_rows
+    call = lambda bias=A + 300 * MB, z=A, out=A + 100 * MB, ws=A + 200 * MB: f(
+        ctypes.byref(p), ctypes.byref(w), z, bias, out, ws, 1 << 40, None)
+    assert call(bias=None) == -1
+    assert call(bias=A + 300 * MB + 4) == -6
+    assert call(out=A + 300 * MB) == -7          # out on the bias
+    assert call(ws=A + 300 * MB) == -7           # workspace on the bias
+    q = prob(I=64, rows=65)
+    assert f(ctypes.byref(q), ctypes.byref(w), A, A + 300 * MB, A + 100 * MB, A + 200 * MB, 1 << 40, None) == -2
+
+
+def test_pair_bias_reject(lib):
+    w = weights()
+    f = lib.triangle_attn_pair_bias
+    p = prob(I=64, rows=16)
+    assert f(ctypes.byref(p), ctypes.byref(w), A, -1, A + 100 * MB, None) == -2
+    assert f(ctypes.byref(p), ctypes.byref(w), A, 49, A + 100 * MB, None) == -2
+    assert f(ctypes.byref(p), ctypes.byref(w), None, 0, A + 100 * MB, None) == -1
+    assert f(ctypes.byref(p), ctypes.byref(w), A, 0, None, None) == -1
+    assert f(ctypes.byref(p), ctypes.byref(w), A, 0, A + 100 * MB + 8, None) == -6
+    assert f(ctypes.byref(p), ctypes.byref(w), A, 0, A + 1024, None) == -7  # bias over z
+
+
+def test_stage_entries_reject(lib):
+    w = weights()
+    p = prob()
+    rc, lay = layout(lib, p, ta.TA_START)
+    assert lib.triangle_attn_project(ctypes.byref(p), ta.TA_START, ctypes.byref(w), A, A + 200 * MB,
+                                     lay.total - 1, None) == -5
+    assert lib.triangle_attn_project(ctypes.byref(p), 5, ctypes.byref(w), A, A + 200 * MB, lay.total, None) == -9
+    # start/end keep their bias in the workspace: passing one is a variant error
+    assert lib.triangle_attn_attend(ctypes.byref(p), ta.TA_START, ctypes.byref(w), A + 300 * MB, A + 100 * MB,
+                                    A + 200 * MB, lay.total, None) == -9
+    pr = prob(I=64, rows=8)
+    rc, lr = layout(lib, pr, ta.TA_ROWS)
+    assert lib.triangle_attn_attend(ctypes.byref(pr), ta.TA_ROWS, ctypes.byref(w), None, A + 100 * MB,
+                                    A + 200 * MB, lr.total, None) == -1
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    z = torch.zeros(4, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ta.triangle_attn_start(z, {})

@@ -411,3 +411,20 @@ def test_planted_mistake_is_caught(monkeypatch, name, mut):
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(True)
     assert any(caught), f"mutant {mut.__name__} of {name} passed every pin"
+
+
+def test_rows_queries_is_restriction_of_rows_start_and_end():
+    rng = np.random.default_rng(18)
+    p = rand_params(rng, 128, 4, 32, gamma_beta=True, b_g=True)
+    I = 11
+    z = rand_z(rng, I, 128)
+    js = [0, 4, 10]
+    full = ref.triangle_attn_start(z, p)
+    got = ref.triangle_attn_rows_queries(z[[2, 7]], ref.pair_bias(z[js], p), js, p)
+    assert np.abs(got - full[[2, 7]][:, js]).max() <= 1e-12
+    # ending node: line = column j, queries = rows i, bias of query i against key k is b_ki
+    full_end = ref.triangle_attn_end(z, p)
+    is_ = [1, 9]
+    bias_q = ref.pair_bias(np.transpose(z[:, is_], (1, 0, 2)), p)  # [h][n][k] = b(z[k, i_n])
+    got = ref.triangle_attn_rows_queries(np.transpose(z[:, [3, 6]], (1, 0, 2)), bias_q, is_, p)
+    assert np.abs(got - np.transpose(full_end[is_][:, [3, 6]], (1, 0, 2))).max() <= 1e-12

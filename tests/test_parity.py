@@ -1,0 +1,316 @@
+"""GPU parity: the HIP library (through the C ABI) against the float64 oracle.
+
+Tolerances (compared element by element on the stored outputs, upcast exactly):
+  bf16 inputs, fp32 accumulation: max |gpu - ref| <= 2e-2 and
+                                  sum |gpu - ref| / sum |ref| <= 5e-3
+  fp32:                           max |gpu - ref| <= 1e-5
+Small and ragged sizes are compared on every output; the five workload sizes
+are compared on sampled rows/columns that the oracle evaluates one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+from protein_pair_representation_amd import inputs
+from protein_pair_representation_amd import triattn as ta
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS, BF16_REL_L1, F32_MAX_ABS = 2e-2, 5e-3, 1e-5
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check(gpu, want, dtype, what=""):
+    got = inputs.to_f64(gpu)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - want)
+    if dtype == "f32":
+        assert err.max() <= F32_MAX_ABS, f"{what}: max abs {err.max():.3e}"
+    else:
+        rel = err.sum() / max(np.abs(want).sum(), 1e-300)
+        assert err.max() <= BF16_MAX_ABS and rel <= BF16_REL_L1, f"{what}: max abs {err.max():.3e}, rel L1 {rel:.3e}"
+    return float(err.max())
+
+
+def weights_with_extras(seed, dtype, extras=True):
+    """Seeded weights; with extras the LayerNorm affine and both biases are non-trivial."""
+    w = inputs.make_weights(seed, dtype)
+    if extras:
+        g = torch.Generator().manual_seed(seed)
+        w["ln_gamma"] = 1.0 + 0.2 * torch.randn(128, generator=g)
+        w["ln_beta"] = 0.1 * torch.randn(128, generator=g)
+        w["b_g"] = 0.5 * torch.randn(128, generator=g)
+        w["b_o"] = 0.1 * torch.randn(128, generator=g)
+    return w
+
+
+def dev(w):
+    return {k: v.cuda() for k, v in w.items()}
+
+
+def params64(w):
+    return ref.params(inputs.weights_f64(w), 4, 32, 1e-5)
+
+
+def guarded(shape, dtype, margin=4096):
+    """A tensor with guard bands on both sides, filled with a sentinel; returns (buffer, view)."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * margin,), 7.0, dtype=dtype, device="cuda")
+    return buf, buf[margin:margin + n].view(shape)
+
+
+def guards_intact(buf, margin=4096):
+    return bool(torch.all(buf[:margin] == 7.0)) and bool(torch.all(buf[-margin:] == 7.0))
+
+
+# ------------------------------------------------------------------ small and ragged sizes, full output
+
+SMALL = [(1, "bf16"), (5, "bf16"), (63, "bf16"), (64, "f32"), (65, "bf16"), (65, "f32"), (130, "bf16"),
+         (200, "f32"), (257, "bf16")]
+
+
+@pytest.mark.parametrize("I,dtype", SMALL)
+@pytest.mark.parametrize("variant", ["start", "end"])
+def test_small_full(I, dtype, variant):
+    say(f"[parity] {variant} I={I} {dtype}")
+    w = weights_with_extras(100 + I, dtype)
+    z = inputs.make_z(100 + I, I, dtype)
+    buf, out = guarded((I, I, 128), TDT[dtype])
+    fn = ta.triangle_attn_start if variant == "start" else ta.triangle_attn_end
+    fn(z.cuda(), dev(w), out=out)
+    torch.cuda.synchronize()
+    assert guards_intact(buf), "write outside the output"
+    f = ref.triangle_attn_start if variant == "start" else ref.triangle_attn_end
+    check(out, f(inputs.to_f64(z), params64(w)), dtype, f"{variant} I={I}")
+
+
+@pytest.mark.parametrize("I,R,dtype", [(5, 3, "bf16"), (130, 1, "f32"), (130, 64, "bf16"), (257, 33, "bf16")])
+def test_rows_given_bias(I, R, dtype):
+    """Row block with a caller-supplied fp32 bias carrying large per-query offsets."""
+    say(f"[parity] rows I={I} R={R} {dtype}")
+    w = weights_with_extras(200 + I, dtype)
+    zr = inputs.make_z_rows(200 + I, I, 7 % I, R, dtype)
+    offs = np.linspace(-30, 30, I)
+    bias = inputs.random_bias(I, 4, I, scale=2.0, offset_per_query=offs)
+    buf, out = guarded((R, I, 128), TDT[dtype])
+    ta.triangle_attn_start_rows(zr.cuda(), bias.cuda(), dev(w), out=out)
+    torch.cuda.synchronize()
+    assert guards_intact(buf)
+    check(out, ref.triangle_attn_rows(inputs.to_f64(zr), inputs.to_f64(bias), params64(w)), dtype, "rows")
+
+
+@pytest.mark.parametrize("I,R,row0,dtype", [(5, 2, 3, "bf16"), (130, 40, 17, "bf16"), (200, 200, 0, "f32")])
+def test_pair_bias(I, R, row0, dtype):
+    say(f"[parity] pair_bias I={I} R={R} row0={row0} {dtype}")
+    w = weights_with_extras(300 + I, dtype)
+    zr = inputs.make_z_rows(300 + I, I, row0, R, dtype)
+    bbuf = torch.full((4 * I * I + 2 * 4096,), 7.0, dtype=torch.float32, device="cuda")
+    bias = bbuf[4096:4096 + 4 * I * I].view(4, I, I)
+    ta.triangle_attn_pair_bias(zr.cuda(), dev(w), row0=row0, bias=bias)
+    torch.cuda.synchronize()
+    assert guards_intact(bbuf)
+    got = inputs.to_f64(bias)
+    want = ref.pair_bias(inputs.to_f64(zr), params64(w))
+    # bf16: LayerNorm output is rounded to bf16 before the projection
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert np.abs(got[:, row0:row0 + R] - want).max() <= tol
+    untouched = np.ones(I, bool)
+    untouched[row0:row0 + R] = False
+    assert np.all(got[:, untouched] == 7.0)
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+
+def test_end_is_transposed_start_bitwise():
+    say("[invariant] end(Z) == start(Z^T)^T")
+    w = dev(weights_with_extras(5, "bf16"))
+    z = inputs.make_z(5, 190, "bf16").cuda()
+    a = ta.triangle_attn_end(z, w)
+    b = ta.triangle_attn_start(z.transpose(0, 1).contiguous(), w).transpose(0, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_rows_equal_start_rows_bitwise():
+    say("[invariant] rows == rows of start")
+    w = dev(weights_with_extras(6, "bf16"))
+    I = 300
+    z = inputs.make_z(6, I, "bf16").cuda()
+    full = ta.triangle_attn_start(z, w)
+    bias = torch.empty((4, I, I), dtype=torch.float32, device="cuda")
+    for r0 in range(0, I, 128):  # bias assembled from row blocks, as a 1D-sharded run would
+        ta.triangle_attn_pair_bias(z[r0:r0 + 128], w, row0=r0, bias=bias)
+    part = ta.triangle_attn_start_rows(z[100:217].contiguous(), bias, w)
+    torch.cuda.synchronize()
+    assert torch.equal(part, full[100:217])
+
+
+def test_repeatable_bitwise():
+    say("[invariant] repeatability")
+    w = dev(weights_with_extras(7, "bf16"))
+    z = inputs.make_z(7, 333, "bf16").cuda()
+    a = ta.triangle_attn_start(z, w)
+    b = ta.triangle_attn_start(z, w)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_gate(dtype):
+    say(f"[invariant] zero gate {dtype}")
+    w = weights_with_extras(8, dtype)
+    w["w_g"] = torch.zeros_like(w["w_g"])
+    w["b_g"] = torch.full((128,), -1e4)
+    w["b_o"] = torch.arange(128, dtype=torch.float32) / 8 - 8   # exact in bf16
+    z = inputs.make_z(8, 77, dtype).cuda()
+    out = ta.triangle_attn_start(z, dev(w))
+    torch.cuda.synchronize()
+    want = w["b_o"].to(TDT[dtype]).cuda().expand(77, 77, 128)
+    assert torch.equal(out, want)
+
+
+def test_output_may_alias_input():
+    say("[invariant] out == z")
+    w = dev(weights_with_extras(9, "bf16"))
+    z = inputs.make_z(9, 100, "bf16").cuda()
+    want = ta.triangle_attn_start(z, w)
+    z2 = z.clone()
+    ta.triangle_attn_start(z2, w, out=z2)
+    torch.cuda.synchronize()
+    assert torch.equal(z2, want)
+
+
+def test_stream_argument():
+    say("[invariant] side stream")
+    w = dev(weights_with_extras(10, "bf16"))
+    z = inputs.make_z(10, 129, "bf16").cuda()
+    want = ta.triangle_attn_start(z, w)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        got = ta.triangle_attn_start(z, w, stream=s)
+    s.synchronize()
+    assert torch.equal(got, want)
+
+
+# ------------------------------------------------------------------ stage 1 against oracle intermediates
+
+@pytest.mark.parametrize("variant,dtype", [("start", "bf16"), ("end", "bf16"), ("start", "f32")])
+def test_projection_stage(variant, dtype):
+    say(f"[stage] project {variant} {dtype}")
+    I = 70
+    w = weights_with_extras(11, dtype)
+    z = inputs.make_z(11, I, dtype)
+    ws = ta.triangle_attn_project(z.cuda(), dev(w), variant=variant)
+    torch.cuda.synchronize()
+    v = {k: inputs.to_f64(t) for k, t in ta.workspace_views(ws, I, I, TDT[dtype], variant).items()}
+    z64 = inputs.to_f64(z)
+    if variant == "end":
+        z64 = np.transpose(z64, (1, 0, 2))  # line = column of Z
+    q, k, vv, g, b = ref.project(z64, params64(w))   # [L][P][H][d], bias [L][P][H]
+    tol = 1e-5 if dtype == "f32" else 3e-2
+    assert np.abs(v["q"][:, :, :I].transpose(0, 2, 1, 3) - q / np.sqrt(32)).max() <= tol
+    assert np.abs(v["k"][:, :, :I].transpose(0, 2, 1, 3) - k).max() <= tol
+    assert np.abs(v["vt"][:, :, :, :I].transpose(0, 3, 1, 2) - vv).max() <= tol
+    assert np.abs(v["g"][:, :, :I].transpose(0, 2, 1, 3) - g).max() <= tol
+    # bias[h][line][pos] = b(token at (line, pos)); for end this is the transposed bias
+    assert np.abs(v["bias"] - np.transpose(b, (2, 0, 1))).max() <= tol
+    assert np.all(np.isfinite(v["q"])) and np.all(np.isfinite(v["vt"]))
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def _workload(name):
+    w = inputs.WORKLOADS[name]
+    return w, inputs.workload_weights(w)
+
+
+@pytest.mark.parametrize("name", ["start-f32-I64", "start-bf16-I384"])
+def test_workload_full(name):
+    say(f"[workload] {name} full")
+    wl, w = _workload(name)
+    z = inputs.workload_z(wl)
+    out = ta.triangle_attn_start(z.cuda(), dev(w))
+    torch.cuda.synchronize()
+    check(out, ref.triangle_attn_start(inputs.to_f64(z), params64(w)), wl.dtype, name)
+
+
+def _sampled_start(z, p, rows_i, js):
+    """oracle out[i][j] for i in rows_i, j in js (bias rows from Z[js])."""
+    js_t = torch.as_tensor(np.asarray(js), dtype=torch.long)
+    bias_q = ref.pair_bias(inputs.to_f64(z[js_t]), p)
+    return ref.triangle_attn_rows_queries(inputs.to_f64(z[list(rows_i)]), bias_q, np.asarray(js), p)
+
+
+@pytest.mark.parametrize("name,variant", [("startend-bf16-I1024-distogram", "start"),
+                                          ("startend-bf16-I1024-distogram", "end"),
+                                          ("start-bf16-I2048-outliers", "start")])
+def test_workload_sampled(name, variant):
+    say(f"[workload] {name} {variant} sampled")
+    wl, w = _workload(name)
+    I = wl.I
+    z = inputs.workload_z(wl)
+    fn = ta.triangle_attn_start if variant == "start" else ta.triangle_attn_end
+    out = fn(z.cuda(), dev(w))
+    torch.cuda.synchronize()
+    p = params64(w)
+    lines = [0, 1, 333, I // 2, I - 1]
+    qs = np.r_[0:64, I // 2 - 7:I // 2 + 9, I - 64:I]
+    if variant == "start":
+        want = _sampled_start(z, p, lines, qs)                     # [line i][query j]
+        got = out[lines][:, torch.as_tensor(qs)]
+    else:
+        zt = z.transpose(0, 1)                                     # line = column j of Z
+        want = _sampled_start(zt, p, lines, qs)                    # [column j][row i]
+        got = out[torch.as_tensor(qs)][:, lines].transpose(0, 1)
+    check(got.cpu(), want, wl.dtype, f"{name} {variant}")
+    assert torch.isfinite(out).all()
+
+
+def _row_ranges(wl, qs):
+    """Rows qs of the workload's Z, generated by consecutive runs."""
+    parts, start = [], 0
+    qs = list(qs)
+    while start < len(qs):
+        end = start
+        while end + 1 < len(qs) and qs[end + 1] == qs[end] + 1:
+            end += 1
+        parts.append(inputs.workload_z(wl, qs[start], qs[end] - qs[start] + 1))
+        start = end + 1
+    return torch.cat(parts)
+
+
+def test_workload_rows_4096():
+    name = "rows-bf16-R1024-I4096"
+    say(f"[workload] {name} sampled")
+    wl, w = _workload(name)
+    I, R = wl.I, wl.n_rows
+    wd = dev(w)
+    bias = torch.empty((4, I, I), dtype=torch.float32, device="cuda")
+    host_rows, dev_rows = [], []
+    for r0 in range(0, I, 512):                                    # whole bias, built block by block
+        zb = inputs.workload_z(wl, r0, 512)
+        zbd = zb.cuda()
+        ta.triangle_attn_pair_bias(zbd, wd, row0=r0, bias=bias)
+        if r0 < R:
+            host_rows.append(zb)
+            dev_rows.append(zbd)
+        say(f"  bias rows {r0}..{r0 + 511} enqueued")
+    z_rows_dev = torch.cat(dev_rows)
+    out = ta.triangle_attn_start_rows(z_rows_dev, bias, wd)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    p = params64(w)
+    lines = [0, 517, R - 1]
+    qs = np.r_[0:32, 2000:2040, I - 32:I]
+    bias_q = ref.pair_bias(inputs.to_f64(_row_ranges(wl, qs)), p)
+    z_lines = torch.cat(host_rows)[lines]
+    want = ref.triangle_attn_rows_queries(inputs.to_f64(z_lines), bias_q, qs, p)
+    got = out[lines][:, torch.as_tensor(qs)]
+    check(got.cpu(), want, wl.dtype, name)
