@@ -37,8 +37,7 @@
  *  - No global mutable state: calls are thread-safe; calls that share a
  *    workspace must be ordered by the caller (same stream or events).
  *  - Supported shapes: c_z = 128, heads * head_dim = 128, head_dim = 32, any
- *    I >= 1 (ragged tails handled), 1 <= rows <= I.  I * I * max(c_z, ...) must
- *    fit the 32-bit element offsets used internally: I <= 16384.
+ *    1 <= I <= 65536 (ragged tails handled), 1 <= rows <= I.
  */
 #ifndef TRIATTN_H
 #define TRIATTN_H
@@ -101,15 +100,30 @@ typedef struct ta_weights {
 /* Byte offsets of the intermediates inside a workspace, and their layouts.
  * L = lines (rows of Z for start/rows, columns of Z for end), P = positions
  * padded to a multiple of 128 (padding holds finite values).
- *   q    cdt  [L][H][P][d]   query, already multiplied by 1/sqrt(d)
+ *   q    cdt  [L][H][P][d]   query multiplied by log2(e)/sqrt(d)
  *   k    cdt  [L][H][P][d]
  *   vt   cdt  [L][H][d][P]   value, transposed per head
  *   g    cdt  [L][H][P][d]   gate after the sigmoid
- *   bias fp32 [H][I][I]      start/end only (absent for the row block);
- *                            end stores the transposed bias b_ki at [h][i][k]
- * For the end variant line = column j of Z and position = row i.           */
+ *   bias bdt  H*P*P          the packed bias the attention kernel reads (bdt =
+ *                            fp16 for TA_BF16, fp32 for TA_F32): per
+ *                            query row shifted by its maximum over keys, times
+ *                            log2(e), in tiles of 32 queries x 64 keys (2048
+ *                            elements; tile (h, j/32, k/64) at
+ *                            ((h*P/32 + j/32)*P/64 + k/64)*2048); inside a tile,
+ *                            with k%64 = 16g + 8hh + t, element (j, k) is at
+ *                            g*512 + (j%32 + 32*hh)*8 + t.  Keys >= I hold
+ *                            -30000 (exp2 of it is 0), query rows >= I filler.
+ *                            The end variant holds the transposed bias b_ki at
+ *                            (h, i, k); the row block holds the caller's bias.
+ *   bias_f32 fp32 [H][I][I]  start/end only: the pair bias as K1 computes it,
+ *                            bias_f32[h][line][pos] = b^h of token (line, pos),
+ *                            natural-log units (absent, (size_t)-1, for rows)
+ * For the end variant line = column j of Z and position = row i.
+ * The attention kernel works in base 2 on shifted logits: exp2(q.k + bias - m)
+ * is the softmax numerator exp(q.k/sqrt(d) + b) up to a factor common to the
+ * query's row, which the normalisation removes.                              */
 typedef struct ta_ws_layout {
-  size_t q, k, vt, g, bias; /* byte offsets; bias = (size_t)-1 when absent */
+  size_t q, k, vt, g, bias, bias_f32; /* byte offsets */
   size_t total;             /* bytes required */
   int32_t lines, positions; /* L and padded P */
 } ta_ws_layout;
@@ -143,7 +157,9 @@ int triangle_attn_end(const ta_problem* prob, const ta_weights* w, const void* z
  *   z_rows cdt  [R][I][c_z]   R consecutive rows of Z
  *   bias   fp32 [H][I][I]     the whole pair bias, bias[h][j][k] = b_jk^h (e.g. built
  *                             with triangle_attn_pair_bias); rows are independent,
- *                             so the global offset of the block is not needed
+ *                             so the global offset of the block is not needed.
+ *                             A key can be masked with -inf (any value below
+ *                             -2.0e4 acts as -2.0e4: its softmax weight is 0)
  *   out    cdt  [R][I][c_z]
  *   ws     at least triangle_attn_workspace_layout(TA_ROWS).total bytes */
 int triangle_attn_start_rows(const ta_problem* prob, const ta_weights* w, const void* z_rows,
@@ -165,7 +181,9 @@ int triangle_attn_project(const ta_problem* prob, int variant, const ta_weights*
 
 /* Stage 2 alone: fused attention + gate + output projection from a workspace
  * filled by triangle_attn_project with the same problem and variant.  `bias`
- * is required for TA_ROWS and must be NULL otherwise (the workspace holds it). */
+ * is required for TA_ROWS (natural-log units, [H][I][I]; it is first copied,
+ * scaled by log2(e), into the workspace) and must be NULL otherwise (the
+ * workspace already holds it). */
 int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* w,
                          const float* bias, void* out, const void* ws, size_t ws_bytes,
                          void* stream);

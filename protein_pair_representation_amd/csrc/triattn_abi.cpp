@@ -51,14 +51,16 @@ void layout_of(const ta_problem* p, int variant, ta_ws_layout* l) {
   l->k = region;
   l->vt = 2 * region;
   l->g = 3 * region;
-  size_t total = 4 * region;
-  if (variant == TA_ROWS) {
-    l->bias = (size_t)-1;
-  } else {
-    l->bias = total;
-    total += align256((size_t)kHeads * p->I * p->I * sizeof(float));
+  // every variant: the packed bias the attention kernel reads (tiled, compute dtype)
+  l->bias = 4 * region;
+  const size_t packed = align256((size_t)kHeads * P * P * esize(p->dtype));
+  if (variant == TA_ROWS) {  // the caller supplies the fp32 bias
+    l->bias_f32 = (size_t)-1;
+    l->total = l->bias + packed;
+  } else {                   // K1 writes the fp32 bias here, then it is packed
+    l->bias_f32 = l->bias + packed;
+    l->total = l->bias_f32 + align256((size_t)kHeads * p->I * p->I * sizeof(float));
   }
-  l->total = total;
 }
 
 int check_weights(const ta_weights* w) {
@@ -113,7 +115,7 @@ triattn::ProjectArgs project_args(const ta_problem* p, int variant, const ta_wei
   a.k = base + l.k;
   a.vt = base + l.vt;
   a.g = base + l.g;
-  a.bias = variant == TA_ROWS ? nullptr : (float*)(base + l.bias);
+  a.bias = variant == TA_ROWS ? nullptr : (float*)(base + l.bias_f32);
   a.bias_row0 = 0;
   a.I = p->I;
   a.P = l.positions;
@@ -131,7 +133,8 @@ triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weigh
   a.k = base + l.k;
   a.vt = base + l.vt;
   a.g = base + l.g;
-  a.bias = variant == TA_ROWS ? bias : (const float*)(base + l.bias);
+  (void)bias;  // the row-block bias is first scaled into the workspace (scale_rows_bias)
+  a.bias = (const void*)(base + l.bias);
   a.w_o = w->w_o;
   a.b_o = w->b_o;
   a.out = out;
@@ -144,6 +147,14 @@ triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weigh
 }
 
 int enqueue(hipError_t e) { return e == hipSuccess ? TA_OK : TA_ERR_HIP; }
+
+// fp32 bias (the caller's for the row block, K1's otherwise) -> the packed
+// tiled bias the attention kernel reads.
+int pack_bias(const ta_problem* p, int variant, const float* caller_bias, void* ws, const ta_ws_layout& l,
+              hipStream_t s) {
+  const float* src = variant == TA_ROWS ? caller_bias : (const float*)((char*)ws + l.bias_f32);
+  return enqueue(triattn::launch_pack_bias(src, (char*)ws + l.bias, p->I, l.positions, p->dtype, s));
+}
 
 // Shared driver of start / end / rows.
 int run_full(const ta_problem* p, int variant, const ta_weights* w, const void* z, const float* bias,
@@ -165,6 +176,7 @@ int run_full(const ta_problem* p, int variant, const ta_weights* w, const void* 
   (void)hipGetLastError();  // clear a stale error so that only our launches are reported
   triattn::ProjectArgs pa = project_args(p, variant, w, z, ws, l);
   if ((rc = enqueue(triattn::launch_project(pa, p->dtype, s)))) return rc;
+  if ((rc = pack_bias(p, variant, bias, ws, l, s))) return rc;
   triattn::AttendArgs aa = attend_args(p, variant, w, bias, out, ws, l);
   return enqueue(triattn::launch_attend(aa, p->dtype, s));
 }
@@ -254,7 +266,9 @@ int triangle_attn_project(const ta_problem* prob, int variant, const ta_weights*
   if (overlap({ws, l.total}, {z, tok_bytes})) return TA_ERR_ALIAS;
   (void)hipGetLastError();
   triattn::ProjectArgs a = project_args(prob, variant, w, z, ws, l);
-  return enqueue(triattn::launch_project(a, prob->dtype, (hipStream_t)stream));
+  if ((rc = enqueue(triattn::launch_project(a, prob->dtype, (hipStream_t)stream)))) return rc;
+  if (variant == TA_ROWS) return TA_OK;  // the row block's bias arrives with the attention stage
+  return pack_bias(prob, variant, nullptr, ws, l, (hipStream_t)stream);
 }
 
 int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* w, const float* bias, void* out,
@@ -273,6 +287,7 @@ int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* 
   const Span bspan = {bias, bias ? (size_t)kHeads * prob->I * prob->I * sizeof(float) : 0};
   if ((rc = check_out_alias(prob, w, {out, tok_bytes}, {nullptr, 0}, {ws, l.total}, bspan))) return rc;
   (void)hipGetLastError();
+  if (variant == TA_ROWS && (rc = pack_bias(prob, variant, bias, (void*)ws, l, (hipStream_t)stream))) return rc;
   triattn::AttendArgs a = attend_args(prob, variant, w, bias, out, ws, l);
   return enqueue(triattn::launch_attend(a, prob->dtype, (hipStream_t)stream));
 }

@@ -16,7 +16,7 @@ struct ProjectArgs {
   const void *w_q, *w_k, *w_v, *w_g, *w_b;
   const float* b_g;
   void *q, *k, *vt, *g;   // workspace regions (unused when bias_only)
-  float* bias;            // [H][I][I] or nullptr
+  float* bias;            // plain fp32 [H][I][I] (natural-log units), or nullptr
   int bias_row0;          // bias row of line 0
   int I, P, lines;
   int bias_only;
@@ -25,7 +25,7 @@ struct ProjectArgs {
 // K2: fused attention over `lines` lines of `I` keys, queries in blocks of 128.
 struct AttendArgs {
   const void *q, *k, *vt, *g;
-  const float* bias;      // [H][I][I]
+  const void* bias;       // tiled workspace layout (bias_tiled_index), compute dtype, base-2 units, keys >= I -30000
   const void* w_o;
   const float* b_o;       // or nullptr
   void* out;
@@ -35,5 +35,8 @@ struct AttendArgs {
 
 hipError_t launch_project(const ProjectArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& a, int dtype, hipStream_t stream);
+// tiled dst(h, j, k) = max((src[h][j][k] - max_k src[h][j][k]) * log2(e), -30000) in the
+// compute dtype; keys >= I -30000, query rows >= I zero
+hipError_t launch_pack_bias(const float* src, void* dst, int I, int P, int dtype, hipStream_t stream);
 
 }  // namespace triattn

@@ -37,7 +37,8 @@ class TaWeights(ctypes.Structure):
 
 class TaWsLayout(ctypes.Structure):
     _fields_ = [("q", ctypes.c_size_t), ("k", ctypes.c_size_t), ("vt", ctypes.c_size_t),
-                ("g", ctypes.c_size_t), ("bias", ctypes.c_size_t), ("total", ctypes.c_size_t),
+                ("g", ctypes.c_size_t), ("bias", ctypes.c_size_t), ("bias_f32", ctypes.c_size_t),
+                ("total", ctypes.c_size_t),
                 ("lines", ctypes.c_int32), ("positions", ctypes.c_int32)]
 
 
@@ -236,6 +237,8 @@ def workspace_views(ws: torch.Tensor, I: int, rows: int, dtype: torch.dtype, var
         "vt": view(lay.vt, (L, HEADS, HEAD_DIM, P), dtype, n, es),
         "g": view(lay.g, (L, HEADS, P, HEAD_DIM), dtype, n, es),
     }
+    bdt = torch.float16 if dtype == torch.bfloat16 else torch.float32   # packed bias element type
+    v["bias_tiles"] = view(lay.bias, (HEADS * P * P,), bdt, HEADS * P * P, es)
     if variant != "rows":
-        v["bias"] = view(lay.bias, (HEADS, I, I), torch.float32, HEADS * I * I, 4)
+        v["bias_f32"] = view(lay.bias_f32, (HEADS, I, I), torch.float32, HEADS * I * I, 4)
     return v

@@ -87,11 +87,13 @@ def test_layout_sizes(lib, I, rows, variant, dtype):
     region = (lines * 4 * P * 32 * es + 255) // 256 * 256
     assert lay.lines == lines and lay.positions == P
     assert (lay.q, lay.k, lay.vt, lay.g) == (0, region, 2 * region, 3 * region)
+    assert lay.bias == 4 * region
+    packed = (4 * P * P * es + 255) // 256 * 256
     if variant == ta.TA_ROWS:
-        assert lay.bias == ctypes.c_size_t(-1).value and lay.total == 4 * region
+        assert lay.bias_f32 == ctypes.c_size_t(-1).value and lay.total == 4 * region + packed
     else:
-        assert lay.bias == 4 * region
-        assert lay.total == 4 * region + (4 * I * I * 4 + 255) // 256 * 256
+        assert lay.bias_f32 == 4 * region + packed
+        assert lay.total == lay.bias_f32 + (4 * I * I * 4 + 255) // 256 * 256
 
 
 def _start(lib, p=None, w="default", z=A, out=A + 100 * MB, ws=A + 200 * MB, ws_bytes=1 << 40, fn="start"):

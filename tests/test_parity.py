@@ -201,6 +201,13 @@ def test_stream_argument():
 
 # ------------------------------------------------------------------ stage 1 against oracle intermediates
 
+def untile_bias(raw, P):
+    """[H][P][P] from the workspace's tiled bias layout (documented in include/triattn.h)."""
+    t = raw.reshape(4, P // 32, P // 64, 4, 2, 32, 8)        # h, jb, kb, g, hh, jj, t
+    t = t.transpose(0, 1, 5, 2, 3, 4, 6)                      # h, jb, jj, kb, g, hh, t
+    return t.reshape(4, P, P)
+
+
 @pytest.mark.parametrize("variant,dtype", [("start", "bf16"), ("end", "bf16"), ("start", "f32")])
 def test_projection_stage(variant, dtype):
     say(f"[stage] project {variant} {dtype}")
@@ -215,12 +222,24 @@ def test_projection_stage(variant, dtype):
         z64 = np.transpose(z64, (1, 0, 2))  # line = column of Z
     q, k, vv, g, b = ref.project(z64, params64(w))   # [L][P][H][d], bias [L][P][H]
     tol = 1e-5 if dtype == "f32" else 3e-2
-    assert np.abs(v["q"][:, :, :I].transpose(0, 2, 1, 3) - q / np.sqrt(32)).max() <= tol
+    log2e = 1.0 / np.log(2.0)
+    assert np.abs(v["q"][:, :, :I].transpose(0, 2, 1, 3) - q * log2e / np.sqrt(32)).max() <= tol
     assert np.abs(v["k"][:, :, :I].transpose(0, 2, 1, 3) - k).max() <= tol
     assert np.abs(v["vt"][:, :, :, :I].transpose(0, 3, 1, 2) - vv).max() <= tol
     assert np.abs(v["g"][:, :, :I].transpose(0, 2, 1, 3) - g).max() <= tol
-    # bias[h][line][pos] = b(token at (line, pos)); for end this is the transposed bias
-    assert np.abs(v["bias"] - np.transpose(b, (2, 0, 1))).max() <= tol
+    # bias[h][line][pos] = log2(e) b(token at (line, pos)); for end this is the transposed bias
+    # K1's fp32 bias: bias_f32[h][line][pos] = b(token at (line, pos)) (end: transposed bias)
+    bt = np.transpose(b, (2, 0, 1))
+    assert np.abs(v["bias_f32"] - bt).max() <= (1e-5 if dtype == "f32" else 2e-2)
+    # packed bias: per query row shifted by its maximum, base 2, compute dtype, tiled
+    lay = ta.triangle_attn_workspace_layout(I, I, TDT[dtype], variant)
+    packed = untile_bias(v["bias_tiles"], lay.positions)
+    f32b = v["bias_f32"]
+    want = (f32b - f32b.max(axis=2, keepdims=True)) * log2e
+    rel = 1e-6 if dtype == "f32" else 2.0 ** -10  # fp16: round to nearest of 11 significant bits
+    assert np.all(np.abs(packed[:, :I, :I] - want) <= rel * np.abs(want) + 1e-5)
+    assert np.all(packed[:, :(I + 31) // 32 * 32, I:] <= -29000.0)
+    assert np.all(np.isfinite(packed[:, I:(I + 31) // 32 * 32, :I]))
     assert np.all(np.isfinite(v["q"])) and np.all(np.isfinite(v["vt"]))
 
 
