@@ -99,11 +99,13 @@ typedef struct ta_weights {
 
 /* Byte offsets of the intermediates inside a workspace, and their layouts.
  * L = lines (rows of Z for start/rows, columns of Z for end), P = positions
- * padded to a multiple of 128 (padding holds finite values).
+ * padded to a multiple of 256 (padding holds finite values).
  *   q    cdt  [L][H][P][d]   query multiplied by log2(e)/sqrt(d)
  *   k    cdt  [L][H][P][d]
  *   vt   cdt  [L][H][d][P]   value, transposed per head
  *   g    cdt  [L][H][P][d]   gate after the sigmoid
+ *   o    cdt  [L][H][P][d]   attention output of each head, normalised and
+ *                            gated (written by the attention stage)
  *   bias bdt  H*P*P          the packed bias the attention kernel reads (bdt =
  *                            fp16 for TA_BF16, fp32 for TA_F32): per
  *                            query row shifted by its maximum over keys, times
@@ -123,7 +125,7 @@ typedef struct ta_weights {
  * is the softmax numerator exp(q.k/sqrt(d) + b) up to a factor common to the
  * query's row, which the normalisation removes.                              */
 typedef struct ta_ws_layout {
-  size_t q, k, vt, g, bias, bias_f32; /* byte offsets */
+  size_t q, k, vt, g, o, bias, bias_f32; /* byte offsets */
   size_t total;             /* bytes required */
   int32_t lines, positions; /* L and padded P */
 } ta_ws_layout;

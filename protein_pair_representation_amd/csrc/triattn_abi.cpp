@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kCz = 128, kHeads = 4, kHeadDim = 32, kPosAlign = 128, kMaxI = 65536;
+constexpr int kCz = 128, kHeads = 4, kHeadDim = 32, kPosAlign = 256, kMaxI = 65536;
 
 size_t esize(int dtype) { return dtype == TA_BF16 ? 2 : 4; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -51,8 +51,9 @@ void layout_of(const ta_problem* p, int variant, ta_ws_layout* l) {
   l->k = region;
   l->vt = 2 * region;
   l->g = 3 * region;
-  // every variant: the packed bias the attention kernel reads (tiled, compute dtype)
-  l->bias = 4 * region;
+  l->o = 4 * region;
+  // every variant: the packed bias the attention kernel reads (tiled)
+  l->bias = 5 * region;
   const size_t packed = align256((size_t)kHeads * P * P * esize(p->dtype));
   if (variant == TA_ROWS) {  // the caller supplies the fp32 bias
     l->bias_f32 = (size_t)-1;
@@ -133,7 +134,8 @@ triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weigh
   a.k = base + l.k;
   a.vt = base + l.vt;
   a.g = base + l.g;
-  (void)bias;  // the row-block bias is first scaled into the workspace (scale_rows_bias)
+  a.o = (void*)(base + l.o);
+  (void)bias;  // the row-block bias is first packed into the workspace (pack_bias)
   a.bias = (const void*)(base + l.bias);
   a.w_o = w->w_o;
   a.b_o = w->b_o;
@@ -141,7 +143,6 @@ triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weigh
   a.I = p->I;
   a.P = l.positions;
   a.lines = l.lines;
-  a.nqb = l.positions / kPosAlign;
   a.out_transposed = variant == TA_END ? 1 : 0;
   return a;
 }

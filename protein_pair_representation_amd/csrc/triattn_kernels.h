@@ -22,14 +22,17 @@ struct ProjectArgs {
   int bias_only;
 };
 
-// K2: fused attention over `lines` lines of `I` keys, queries in blocks of 128.
+// K2: fused attention over `lines` lines of `I` keys; P (the padded position
+// count) must be a multiple of 256.
 struct AttendArgs {
   const void *q, *k, *vt, *g;
+  void* o;                // workspace: gated, normalised head outputs, same layout as q
   const void* bias;       // tiled workspace layout (bias_tiled_index), compute dtype, base-2 units, keys >= I -30000
   const void* w_o;
   const float* b_o;       // or nullptr
   void* out;
-  int I, P, lines, nqb;
+  int I, P, lines;
+  int nqb;                // query blocks (set by launch_attend from the block width)
   int out_transposed;     // 1: out[j][line], 0: out[line][j]
 };
 

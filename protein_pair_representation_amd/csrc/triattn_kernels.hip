@@ -300,21 +300,33 @@ __global__ void __launch_bounds__(NTHREADS) tri_project(ProjectArgs a) {
 }
 
 // ================================================================ K2: fused attention
-// Scores arrive from the MFMA already in base-2 units and already shifted by
-// the running maximum: q is stored pre-multiplied by log2(e)/sqrt(d), the bias
-// by log2(e), and one extra 16-deep contraction slice multiplies a unit
-// fragment with a fragment holding -m (m = running maximum, rounded to the
-// compute dtype so that the MFMA adds it exactly).  The softmax of a tile is
-// then just p = exp2(acc), its conversion, and a row sum (dot2 on packed
-// pairs).  m is only moved when a tile's partial sums exceed 2^16 (and on the
-// first tile of every head): then the exact maximum is taken, O and l are
-// rescaled and the tile is re-exponentiated.  In exact arithmetic any shift
-// gives the same softmax; the shift only keeps exp2 in range.
-constexpr float SUM_LIMIT = 65536.0f;
+// Scores arrive from the MFMA in base-2 units: q is stored times log2(e)/sqrt(d)
+// and the packed bias times log2(e), each query row of the bias shifted by its
+// own maximum (the softmax over keys is unchanged by a per-query shift).  After
+// that shift a score is bounded by |q||k|, so the tile softmax is just
+// p = exp2(acc), its conversion, and a row sum (dot2 on packed pairs).
+// A running shift m is only introduced when needed: when the first tile of a
+// head has its maximum outside [-64, 64], or when a tile's partial sums pass
+// 2^64 (far from fp32 overflow).  Then the exact maximum is taken, O and l are
+// rescaled, and from there on one extra 16-deep contraction slice (a unit
+// fragment times a fragment holding -m, m rounded to the compute dtype so the
+// MFMA adds it exactly) subtracts m inside the MFMA.  In exact arithmetic any
+// shift gives the same softmax; the shift only keeps exp2 in range.
+constexpr float SUM_LIMIT = 1.8446744073709552e19f;  // 2^64
+constexpr float FIRST_LIMIT = 64.0f;
 
 template <typename T> __device__ __forceinline__ typename El<T>::frag unit_frag(float v) {
   float t8[8] = {v, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   return to_frag<T>(t8);
+}
+
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+  return xhalf_max(mx);
 }
 
 // p = exp2(s) for the 32 scores of a lane, as MFMA B fragments, and their sum.
@@ -347,27 +359,19 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], typename El<T>::
   return l0 + l1;
 }
 
-// Move the running maximum to the tile's exact maximum (if larger), rescale
-// the accumulators, shift the scores and re-exponentiate.  m is kept exactly
-// representable in T so that the MFMA's -m slice and this code agree.
+// Rare path: move the shift m up to the tile's exact maximum, rescale O and l,
+// shift the scores and re-exponentiate.  Returns the tile sum; d = the amount
+// m moved (scores computed earlier with the old m must be shifted by it too).
 template <typename T>
 __device__ __forceinline__ float rebase_tile(f32x16 (&s)[2], typename El<T>::frag (&pf)[2][2], float& m,
-                                             f32x16& o, float& lsum, bool first) {
-  float mx = s[0][0];
+                                             f32x16& o, float& lsum, float& d) {
+  const float mx = tile_max(s);               // excess of the tile maximum over m
+  const float mnew = (float)(T)(m + fmaxf(mx, 0.f));
+  d = mnew - m;
+  const float alpha = fast_exp2(-d);
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-  mx = xhalf_max(mx);                        // excess of the tile maximum over m
-  float mnew = first ? mx : m + fmaxf(mx, 0.f);
-  mnew = (float)(T)mnew;
-  const float d = mnew - m;
-  if (!first) {
-    const float alpha = fast_exp2(-d);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[i] *= alpha;
-    lsum *= alpha;
-  }
+  for (int i = 0; i < 16; ++i) o[i] *= alpha;
+  lsum *= alpha;
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -376,72 +380,104 @@ __device__ __forceinline__ float rebase_tile(f32x16 (&s)[2], typename El<T>::fra
   return exp_tile<T>(s, pf);
 }
 
-template <typename T>
-__global__ void __launch_bounds__(NTHREADS, 2) tri_attend(AttendArgs a) {
+#ifndef TRIATTN_XCD_MODE
+#define TRIATTN_XCD_MODE 2
+#endif
+
+// Workgroup -> (line group, query block).  Workgroups are dealt to the 8 XCDs
+// round-robin (XCD x runs blocks x, x+8, ...).  Mode 2 (used when the shape
+// allows it) splits the XCDs 4 x 2: XCD x serves the query blocks congruent to
+// x % 4 and one half of the line groups, two query blocks at a time, so the
+// bias slice it reads stays resident in its L2 while each line group's keys and
+// values are read by only 4 XCDs, all walking the lines in step (the first read
+// brings them into the last-level cache for the other three).
+__device__ __forceinline__ void map_block(int bid, int n_lg, int nqb, int& lg, int& qb) {
+  const int mode = TRIATTN_XCD_MODE;
+  if (mode == 2 && nqb % 8 == 0 && n_lg % 2 == 0) {
+    const int x = bid & 7, slot = bid >> 3;
+    const int alpha = x & 3, beta = x >> 2, n_half = n_lg >> 1;
+    const int phase = slot / (2 * n_half), rem = slot - phase * 2 * n_half;
+    lg = beta * n_half + (rem >> 1);
+    qb = alpha + 4 * (2 * phase + (rem & 1));
+  } else if (mode == 1 && nqb % 8 == 0) {
+    const int x = bid & 7, slot = bid >> 3;
+    const int phase = slot / n_lg;
+    lg = slot - phase * n_lg;
+    qb = phase * 8 + x;
+  } else {
+    lg = bid / nqb;
+    qb = bid - lg * nqb;
+  }
+}
+
+// ROWS consecutive lines per workgroup (each wave works on all of them for its
+// 32 queries, so one bias tile serves ROWS rows), WAVES waves = 32*WAVES queries.
+template <typename T, int ROWS, int WAVES, int MIN_WAVES_PER_SIMD>
+__global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(AttendArgs a) {
   typedef typename El<T>::frag frag;
+  typedef typename El<T>::bias_t BT;
+  typedef typename El<T>::bias_frag bfrag;
+  constexpr int NT = WAVES * 64;
   constexpr int KU = HD * El<T>::bytes / 16;      // units per K-tile row (32 channels)
   constexpr int VU = KT * El<T>::bytes / 16;      // units per V^T-tile row (64 keys)
-  constexpr int WU = CZ * El<T>::bytes / 16;      // units per W_o row
   constexpr int KTILE_UNITS = KT * KU;
   constexpr int VTILE_UNITS = HD * VU;
-  constexpr int LD_PER_THREAD = KTILE_UNITS / NTHREADS;  // same for K and V^T tiles
-  __shared__ u32x4 k_lds[2][KTILE_UNITS];
-  __shared__ u32x4 v_lds[2][VTILE_UNITS];
-  // finished heads: per wave, query lr's gated output o[h*32 + e], unit u at u ^ (lr & (WU-1))
-  __shared__ u32x4 o_lds[NTHREADS / 64][32 * WU];
+  constexpr int ROW_UNITS = KTILE_UNITS + VTILE_UNITS;
+  constexpr int STAGE_UNITS = ROWS * ROW_UNITS;
+  static_assert(STAGE_UNITS % NT == 0, "staging must split evenly over the threads");
+  constexpr int LDT = STAGE_UNITS / NT;            // 16-B units staged per thread per tile
+  constexpr int EPU = 16 / El<T>::bytes;           // elements per 16-B unit
+  constexpr int QBW = 32 * WAVES;                  // queries per workgroup
+  __shared__ u32x4 kv_lds[2][STAGE_UNITS];         // [buffer][row][K tile | V^T tile]
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, lr = lane & 31;
   const int I = a.I, P = a.P;
-
-  // XCD-aware order: consecutive logical tiles (same line, neighbouring query
-  // blocks) go to the same XCD so its L2 serves the line's keys and values.
-  const int nblk = gridDim.x;
-  int bid = blockIdx.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int line = bid / a.nqb, qb = bid % a.nqb;
-  const int j = qb * QB + wave * 32 + lr;  // this lane's query
-  const int jc = j < I ? j : I - 1;
-
-  const T* qbase = (const T*)a.q + (size_t)line * NH * P * HD;
-  const T* kbase = (const T*)a.k + (size_t)line * NH * P * HD;
-  const T* vbase = (const T*)a.vt + (size_t)line * NH * HD * P;
-  const T* gbase = (const T*)a.g + (size_t)line * NH * P * HD;
+  const int n_lg = (a.lines + ROWS - 1) / ROWS;
+  int lg, qb;
+  map_block(blockIdx.x, n_lg, a.nqb, lg, qb);
+  const int line0 = lg * ROWS;
+  const int j = qb * QBW + wave * 32 + lr;         // this lane's query
   const int nkt = (I + KT - 1) / KT;
 
-  // K / V^T tile staging: thread tid moves LD_PER_THREAD 16-B units of each.
-  // Addresses are a wave-uniform tile base plus a fixed 32-bit per-lane offset.
-  constexpr int EPU = 16 / El<T>::bytes;  // elements per 16-B unit
-  int k_off[LD_PER_THREAD], v_off[LD_PER_THREAD];
+  // line of row r (rows past the last line repeat it and are never stored)
+  auto line_of = [&](int r) { return line0 + r < a.lines ? line0 + r : a.lines - 1; };
+  const size_t tok_line = (size_t)NH * P * HD;     // q, k, g, o and v^T elements per line
+
+  // staging: thread tid moves LDT units; slot s covers unit tid + s*NT of the stage
+  int g_off[LDT], l_off[LDT];
+  const T* g_base[LDT];
 #pragma unroll
-  for (int s = 0; s < LD_PER_THREAD; ++s) {
-    const int idx = tid + s * NTHREADS;
-    k_off[s] = (idx / KU) * HD + (idx % KU) * EPU;
-    v_off[s] = (idx / VU) * P + (idx % VU) * EPU;
+  for (int s = 0; s < LDT; ++s) {
+    const int idx = tid + s * NT, r = idx / ROW_UNITS, w = idx - r * ROW_UNITS;
+    if (w < KTILE_UNITS) {
+      const int row = w / KU, u = w % KU;
+      g_base[s] = (const T*)a.k + line_of(r) * tok_line;
+      g_off[s] = row * HD + u * EPU;               // + (h*P + kt*KT) * HD
+      l_off[s] = r * ROW_UNITS + row * KU + (u ^ swz<KU>(row));
+    } else {
+      const int ww = w - KTILE_UNITS, e = ww / VU, u = ww % VU;
+      g_base[s] = (const T*)a.vt + line_of(r) * tok_line;
+      g_off[s] = -(e * P + u * EPU) - 1;           // V marker: negative, decoded below
+      l_off[s] = r * ROW_UNITS + KTILE_UNITS + e * VU + (u ^ swz<VU>(e));
+    }
   }
-  u32x4 kreg[LD_PER_THREAD], vreg[LD_PER_THREAD];
+  u32x4 sreg[LDT];
   auto load_tile = [&](int h, int kt) {
 #pragma unroll
-    for (int s = 0; s < LD_PER_THREAD; ++s) {
-      int idx = tid + s * NTHREADS;
-      int r = idx / KU, u = idx % KU;
-      kreg[s] = reinterpret_cast<const u32x4*>(kbase + ((size_t)h * P + kt * KT + r) * HD)[u];
-      int e = idx / VU, uv = idx % VU;
-      vreg[s] = reinterpret_cast<const u32x4*>(vbase + ((size_t)h * HD + e) * P + kt * KT)[uv];
+    for (int s = 0; s < LDT; ++s) {
+      const int off = g_off[s];
+      const T* p = off >= 0 ? g_base[s] + ((size_t)h * P + kt * KT) * HD + off
+                            : g_base[s] + (size_t)h * HD * P + kt * KT + (-off - 1);
+      sreg[s] = *reinterpret_cast<const u32x4*>(p);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int s = 0; s < LD_PER_THREAD; ++s) {
-      int idx = tid + s * NTHREADS;
-      lds_put<KU>(k_lds[buf], idx / KU, idx % KU, kreg[s]);
-      lds_put<VU>(v_lds[buf], idx / VU, idx % VU, vreg[s]);
-    }
+    for (int s = 0; s < LDT; ++s) kv_lds[buf][l_off[s]] = sreg[s];
   };
+
   // bias of a key tile as four B-operand fragments (keys 16g + 8hh + t of this
-  // lane's query): one tiled 32 x 64 block (see bias_tiled_index), four
-  // contiguous per-lane loads
-  typedef typename El<T>::bias_t BT;
-  typedef typename El<T>::bias_frag bfrag;
+  // lane's query): one tiled 32 x 64 block (see bias_tiled_index)
   auto load_bias = [&](const BT* btile, bfrag (&b)[4]) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) b[g] = *reinterpret_cast<const bfrag*>(btile + g * 512 + lane * 8);
@@ -459,137 +495,157 @@ __global__ void __launch_bounds__(NTHREADS, 2) tri_attend(AttendArgs a) {
     esel[g] = to_vec8<bfrag>(v);
   }
   const frag e0 = unit_frag<T>(hh == 0 ? 1.0f : 0.0f);  // contraction slot (0,0) = 1
+  const f32x16 zero = {};
 
-  // this wave's query block; blocks wholly beyond I reuse the last real block
-  const int jb = qb * (QB / 32) + wave, jb_last = (I - 1) >> 5;
+  // this wave's 32-query block; blocks wholly beyond I reuse the last real block
+  const int jb = qb * WAVES + wave, jb_last = (I - 1) >> 5;
   const BT* bias0 = (const BT*)a.bias + ((size_t)(jb < jb_last ? jb : jb_last) * (P >> 6) << 11);
   const size_t bias_head = (size_t)P * P;        // elements per head; key tile stride 2048
 
-  bfrag bias_next[4];                            // bias of the next tile, prefetched
-  load_tile(0, 0);
-  store_tile(0);
-  load_bias(bias0, bias_next);
-  __syncthreads();
+  // global key tile g = h * nkt + kt (past the end: the last tile again, unused)
+  const int ntiles = NH * nkt;
+  auto split = [&](int g, int& h, int& kt) {
+    g = g < ntiles ? g : ntiles - 1;
+    h = g / nkt;
+    kt = g - h * nkt;
+  };
+  bfrag bias_next[4];
+  {
+    load_tile(0, 0);
+    store_tile(0);
+    load_bias(bias0, bias_next);
+    __syncthreads();
+  }
 
-  u32x4* orow_lds = o_lds[wave] + lr * WU;
-  const int oswz = lr & (WU - 1);
-  constexpr int FU = El<T>::bytes / 2;  // 16-B units per 8-element fragment
-  int it = 0;       // flattened (head, key tile) counter; LDS buffer = it & 1
 #pragma unroll 1
   for (int h = 0; h < NH; ++h) {
-    frag qf[2];
+    frag qf[ROWS][2], qm[ROWS];
+    float m[ROWS], lsum[ROWS];
+    f32x16 o[ROWS];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) qf[c] = gld8<T>(qbase + ((size_t)h * P + j) * HD + 16 * c + 8 * hh);
-    float m = 0.f, lsum = 0.f;
-    frag qm = unit_frag<T>(0.f);
-    f32x16 o = {};
-    const BT* brow = bias0 + h * bias_head;      // key tile kt at brow + kt * 2048
+    for (int r = 0; r < ROWS; ++r) {
+      const T* qrow = (const T*)a.q + line_of(r) * tok_line + ((size_t)h * P + j) * HD + 8 * hh;
+      qf[r][0] = gld8<T>(qrow);
+      qf[r][1] = gld8<T>(qrow + 16);
+      qm[r] = unit_frag<T>(0.f);
+      m[r] = 0.f;
+      lsum[r] = 0.f;
+      o[r] = zero;
+    }
 
-    // one key tile: scores, softmax, P.V.  FIRST: the first tile of the head,
-    // which always takes the exact maximum.  bcur holds this tile's bias; the
-    // next tile's is loaded into bnxt.
+    // One key tile for all rows.  The bias scores (two selector products per
+    // 32 keys) are computed once and are the accumulator input of every row's
+    // K Q^T; -m is a last 16-deep slice.  FIRST: the first tile of the head.
     auto tile = [&](int kt, auto first_tag) {
       constexpr bool FIRST = decltype(first_tag)::value;
-      const int buf = it & 1;
-      const bool more = kt + 1 < nkt;
-      const int h_next = more ? h : (h + 1 < NH ? h + 1 : h);
-      const int kt_next = more ? kt + 1 : (h + 1 < NH ? 0 : kt);
-      load_tile(h_next, kt_next);
-      frag kf[2][2], vf[2][2];
+      const int g = h * nkt + kt, buf = g & 1;
+      int hn, ktn;
+      split(g + 1, hn, ktn);
+      load_tile(hn, ktn);                                   // stage the next tile
+      f32x16 sbias[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st) sbias[st] = mma(esel[0], bias_next[2 * st], zero);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) kf[st][c] = lds_frag<T, KU>(k_lds[buf], 32 * st + rho(lr), 2 * c + hh);
+      for (int st = 0; st < 2; ++st) sbias[st] = mma(esel[1], bias_next[2 * st + 1], sbias[st]);
+      load_bias(bias0 + hn * bias_head + ((size_t)ktn << 11), bias_next);
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int r = 0; r < ROWS; ++r) {
+        const u32x4* kl = kv_lds[buf] + r * ROW_UNITS;
+        const u32x4* vl = kl + KTILE_UNITS;
+        frag kf[2][2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) vf[st][c] = lds_frag<T, VU>(v_lds[buf], rho(lr), 4 * st + 2 * hh + c);
-      // s = bias (two selector products per 32 keys) + K Q^T - m
-      f32x16 sc[2];
-      const f32x16 zero = {};
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) sc[st] = mma(esel[0], bias_next[2 * st], zero);
+          for (int c = 0; c < 2; ++c) kf[st][c] = lds_frag<T, KU>(kl, 32 * st + rho(lr), 2 * c + hh);
+        f32x16 sc[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) sc[st] = mma(esel[1], bias_next[2 * st + 1], sc[st]);
-      load_bias(brow + ((size_t)kt_next << 11) + (h_next - h) * bias_head, bias_next);
+        for (int st = 0; st < 2; ++st) sc[st] = mma(kf[st][0], qf[r][0], sbias[st]);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+        for (int st = 0; st < 2; ++st) sc[st] = mma(kf[st][1], qf[r][1], sc[st]);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) sc[st] = mma(kf[st][c], qf[c], sc[st]);
+        for (int st = 0; st < 2; ++st) sc[st] = mma(e0, qm[r], sc[st]);
+        if constexpr (FIRST) {
+          // first tile: shift only if its maximum is far from 0
+          const float mx = tile_max(sc);
+          const float mf = (mx > FIRST_LIMIT || mx < -FIRST_LIMIT) ? (float)(T)mx : 0.f;
+          if (__builtin_amdgcn_ballot_w64(mf != 0.f) != 0) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) sc[st] = mma(e0, qm, sc[st]);
-      frag pf[2][2];
-      float lt;
-      if constexpr (FIRST) {
-        lt = rebase_tile<T>(sc, pf, m, o, lsum, true);
-        qm = unit_frag<T>(hh == 0 ? -m : 0.f);
-      } else {
-        lt = exp_tile<T>(sc, pf);
-        if (__builtin_amdgcn_ballot_w64(!(lt <= SUM_LIMIT)) != 0) {
-          lt = rebase_tile<T>(sc, pf, m, o, lsum, false);
-          qm = unit_frag<T>(hh == 0 ? -m : 0.f);
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) sc[st][i] -= mf;
+            m[r] = mf;
+            qm[r] = unit_frag<T>(hh == 0 ? -mf : 0.f);
+          }
         }
+        frag pf[2][2];
+        float lt = exp_tile<T>(sc, pf);
+        if (__builtin_amdgcn_ballot_w64(!(lt <= SUM_LIMIT)) != 0) {
+          float d;
+          lt = rebase_tile<T>(sc, pf, m[r], o[r], lsum[r], d);
+          qm[r] = unit_frag<T>(hh == 0 ? -m[r] : 0.f);
+        }
+        lsum[r] += lt;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            frag vf = lds_frag<T, VU>(vl, rho(lr), 4 * st + 2 * hh + c);
+            o[r] = mma(vf, pf[st][c], o[r]);
+          }
       }
-      lsum += lt;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) o = mma(vf[st][c], pf[st][c], o);
       store_tile(buf ^ 1);
       __syncthreads();
-      ++it;
     };
 
     tile(0, std::true_type{});
     for (int kt = 1; kt < nkt; ++kt) tile(kt, std::false_type{});
 
-    // ---- finish head h: 1/l, gate
-    const float inv = 1.0f / xhalf_sum(lsum);
-    const T* gp = gbase + ((size_t)h * P + j) * HD + 16 * hh;
-    float gv[16];
-    frag_to_f32<T>(gld8<T>(gp), gv);
-    frag_to_f32<T>(gld8<T>(gp + 8), gv + 8);
-    float ov[16];
+    // ---- finish head h: 1/l, gate; o^T (e = 16*hh + i) to the workspace
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ov[i] = o[i] * inv * gv[i];
-    // o^T fragments of head h (e = 16*hh + 8c + t) kept in LDS until the output projection
+    for (int r = 0; r < ROWS; ++r) {
+      const float inv = 1.0f / xhalf_sum(lsum[r]);
+      const size_t tok = line_of(r) * tok_line + ((size_t)h * P + j) * HD + 16 * hh;
+      float gv[16];
+      frag_to_f32<T>(gld8<T>((const T*)a.g + tok), gv);
+      frag_to_f32<T>(gld8<T>((const T*)a.g + tok + 8), gv + 8);
+      float ov[16];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      frag f = to_frag<T>(ov + 8 * c);
-      u32x4 tmp[FU];
-      __builtin_memcpy(tmp, &f, sizeof(f));
-#pragma unroll
-      for (int s2 = 0; s2 < FU; ++s2) orow_lds[((4 * h + 2 * hh + c) * FU + s2) ^ oswz] = tmp[s2];
+      for (int i = 0; i < 16; ++i) ov[i] = o[r][i] * inv * gv[i];
+      gst8<T>((T*)a.o + tok, to_frag<T>(ov));
+      gst8<T>((T*)a.o + tok + 8, to_frag<T>(ov + 8));
     }
   }
 
   // ---- output projection: out^T[c][j] = sum_(h,e) W_o[c][h*32+e] o^T[h*32+e][j] + b_o[c]
-  T* orow = (T*)a.out + (a.out_transposed ? ((size_t)j * I + line) : ((size_t)line * I + j)) * CZ;
+  // (this lane reads back exactly the o values it wrote)
+#pragma unroll 1
+  for (int r = 0; r < ROWS; ++r) {
+    if (line0 + r >= a.lines) break;
+    const int line = line0 + r;
+    const T* orow_ws = (const T*)a.o + (size_t)line * tok_line + (size_t)j * HD + 16 * hh;
+    T* orow = (T*)a.out + (a.out_transposed ? ((size_t)j * I + line) : ((size_t)line * I + j)) * CZ;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    f32x16 acc;
+    for (int ct = 0; ct < 4; ++ct) {
+      f32x16 acc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = a.b_o ? a.b_o[32 * ct + 16 * hh + i] : 0.f;
-    const T* wrow = (const T*)a.w_o + (size_t)(32 * ct + rho(lr)) * CZ + 16 * hh;
+      for (int i = 0; i < 16; ++i) acc[i] = a.b_o ? a.b_o[32 * ct + 16 * hh + i] : 0.f;
+      const T* wrow = (const T*)a.w_o + (size_t)(32 * ct + rho(lr)) * CZ + 16 * hh;
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
+      for (int hd = 0; hd < NH; ++hd)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        frag wf = gld8<T>(wrow + 32 * h + 8 * c);   // W_o is small and stays in L2
-        u32x4 tmp[FU];
+        for (int c = 0; c < 2; ++c) {
+          frag wf = gld8<T>(wrow + 32 * hd + 8 * c);   // W_o is small and stays in L2
+          frag of = gld8<T>(orow_ws + (size_t)hd * P * HD + 8 * c);
+          acc = mma(wf, of, acc);
+        }
+      if (j < I) {
+        float ov[16];
 #pragma unroll
-        for (int s2 = 0; s2 < FU; ++s2) tmp[s2] = orow_lds[((4 * h + 2 * hh + c) * FU + s2) ^ oswz];
-        frag of;
-        __builtin_memcpy(&of, tmp, sizeof(of));
-        acc = mma(wf, of, acc);
+        for (int i = 0; i < 16; ++i) ov[i] = acc[i];
+        T* p = orow + 32 * ct + 16 * hh;
+        gst8<T>(p, to_frag<T>(ov));
+        gst8<T>(p + 8, to_frag<T>(ov + 8));
       }
-    if (j < I) {
-      float ov[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ov[i] = acc[i];
-      T* p = orow + 32 * ct + 16 * hh;
-      gst8<T>(p, to_frag<T>(ov));
-      gst8<T>(p + 8, to_frag<T>(ov + 8));
     }
   }
 }
@@ -662,12 +718,23 @@ hipError_t launch_pack_bias(const float* src, void* dst, int I, int P, int dtype
   return hipGetLastError();
 }
 
-hipError_t launch_attend(const AttendArgs& a, int dtype, hipStream_t stream) {
-  const long nblk = (long)a.lines * a.nqb;
+#ifndef TRIATTN_ROWS
+#define TRIATTN_ROWS 2
+#endif
+#ifndef TRIATTN_WAVES
+#define TRIATTN_WAVES 4
+#endif
+
+hipError_t launch_attend(const AttendArgs& args, int dtype, hipStream_t stream) {
+  constexpr int R = TRIATTN_ROWS, W = TRIATTN_WAVES;
+  AttendArgs a = args;
+  a.nqb = (a.I + 32 * W - 1) / (32 * W);
+  const long nblk = (long)((a.lines + R - 1) / R) * a.nqb;
+  // bf16: two waves per SIMD; fp32 (twice the fragment registers): one
   if (dtype == 1)
-    hipLaunchKernelGGL(tri_attend<__bf16>, dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL((tri_attend<__bf16, R, W, 2>), dim3((unsigned)nblk), dim3(W * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL(tri_attend<float>, dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL((tri_attend<float, R, W, 1>), dim3((unsigned)nblk), dim3(W * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -37,7 +37,8 @@ class TaWeights(ctypes.Structure):
 
 class TaWsLayout(ctypes.Structure):
     _fields_ = [("q", ctypes.c_size_t), ("k", ctypes.c_size_t), ("vt", ctypes.c_size_t),
-                ("g", ctypes.c_size_t), ("bias", ctypes.c_size_t), ("bias_f32", ctypes.c_size_t),
+                ("g", ctypes.c_size_t), ("o", ctypes.c_size_t), ("bias", ctypes.c_size_t),
+                ("bias_f32", ctypes.c_size_t),
                 ("total", ctypes.c_size_t),
                 ("lines", ctypes.c_int32), ("positions", ctypes.c_int32)]
 
@@ -236,6 +237,7 @@ def workspace_views(ws: torch.Tensor, I: int, rows: int, dtype: torch.dtype, var
         "k": view(lay.k, (L, HEADS, P, HEAD_DIM), dtype, n, es),
         "vt": view(lay.vt, (L, HEADS, HEAD_DIM, P), dtype, n, es),
         "g": view(lay.g, (L, HEADS, P, HEAD_DIM), dtype, n, es),
+        "o": view(lay.o, (L, HEADS, P, HEAD_DIM), dtype, n, es),
     }
     bdt = torch.float16 if dtype == torch.bfloat16 else torch.float32   # packed bias element type
     v["bias_tiles"] = view(lay.bias, (HEADS * P * P,), bdt, HEADS * P * P, es)

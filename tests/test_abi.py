@@ -82,17 +82,17 @@ def test_layout_sizes(lib, I, rows, variant, dtype):
     rc, lay = layout(lib, prob(I, rows, dtype), variant)
     assert rc == 0
     es = 2 if dtype == ta.TA_BF16 else 4
-    P = (I + 127) // 128 * 128
+    P = (I + 255) // 256 * 256
     region = lines = rows if variant == ta.TA_ROWS else I
     region = (lines * 4 * P * 32 * es + 255) // 256 * 256
     assert lay.lines == lines and lay.positions == P
-    assert (lay.q, lay.k, lay.vt, lay.g) == (0, region, 2 * region, 3 * region)
-    assert lay.bias == 4 * region
+    assert (lay.q, lay.k, lay.vt, lay.g, lay.o) == (0, region, 2 * region, 3 * region, 4 * region)
+    assert lay.bias == 5 * region
     packed = (4 * P * P * es + 255) // 256 * 256
     if variant == ta.TA_ROWS:
-        assert lay.bias_f32 == ctypes.c_size_t(-1).value and lay.total == 4 * region + packed
+        assert lay.bias_f32 == ctypes.c_size_t(-1).value and lay.total == 5 * region + packed
     else:
-        assert lay.bias_f32 == 4 * region + packed
+        assert lay.bias_f32 == 5 * region + packed
         assert lay.total == lay.bias_f32 + (4 * I * I * 4 + 255) // 256 * 256
 
 
