@@ -44,7 +44,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int CZ = 128;        // channels per token
 constexpr int NH = 4;          // heads
 constexpr int HD = 32;         // head width
-constexpr int QB = 128;        // queries (positions) per workgroup tile
 constexpr int KT = 64;         // keys per attention tile
 constexpr int NTHREADS = 256;  // 4 waves
 constexpr float LOG2E = 1.4426950408889634f;
@@ -52,6 +51,10 @@ constexpr float LOG2E = 1.4426950408889634f;
 // exactly 0.  It must be finite: the bias enters the scores through a product
 // with a 0/1 selector, and 0 * -inf would be NaN.
 constexpr float MASKED = -30000.0f;
+
+// Word 3 of a raw (stride 0) gfx9 buffer resource: 32-bit data format, no
+// swizzle.  Accesses at offsets >= num_records read 0 / are dropped.
+constexpr int BUF_DWORD3 = 0x00020000;
 
 __device__ __forceinline__ int rho(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
 
@@ -173,24 +176,82 @@ __device__ __forceinline__ typename El<T>::frag lds_frag(const u32x4* base, int 
 }
 
 // ================================================================ K1: LN + projections
-// One workgroup loops over tiles of 128 tokens (one line, 128 consecutive
-// positions); each wave owns 32 tokens.  Lane l holds token rho(l & 31) of its
-// wave and channels 64*(l>>5) .. +63 -- exactly the B-operand fragments of the
-// eight 16-deep contraction slices, with contraction index 64*(l>>5) + 8c + t.
-// The 17 output tiles of 32 channels are q0..3, k0..3, v0..3, g0..3, bias (4 used).
+// A workgroup of WAVES waves loops over tiles of 32*WAVES tokens (one line,
+// consecutive positions); each wave owns 32 of them.  Lane l holds token
+// rho(l & 31) of its wave and, for contraction slice c = 0..7, channels
+// 16c + 8*(l>>5) + t, t = 0..7: exactly its B-operand fragment of slice c.  The
+// other half of the token sits in lane l ^ 32, so the LayerNorm statistics take
+// one cross-half exchange each.  The 17 output tiles of 32 channels (q0..3,
+// k0..3, v0..3, g0..3, and the pair bias with 4 of 32 rows used) are computed
+// four at a time: four independent accumulator chains, so each weight-fragment
+// read overlaps the MFMAs of the other three.  The next tile's tokens are loaded
+// while the current one is computed.
+template <typename T> struct ProjCfg;
+template <> struct ProjCfg<__bf16> {
+  static constexpr int WAVES = 8;          // two waves per SIMD
+  static constexpr bool W_IN_LDS = true;   // 17*32 rows x 256 B = 136 KiB of LDS
+};
+template <> struct ProjCfg<float> {
+  static constexpr int WAVES = 4;
+  static constexpr bool W_IN_LDS = false;  // fp32 weights (272 KiB) are read through the caches
+};
+
+// Weight fragment of output tile mt (rows 32*mt + r, r = rho(lane & 31)),
+// contraction slice c.
+template <typename T, int WUNITS>
+__device__ __forceinline__ typename El<T>::frag proj_wfrag(const u32x4* w_lds, const T* const* wsrc, int mt,
+                                                           int r, int hh, int c) {
+  if constexpr (ProjCfg<T>::W_IN_LDS) {
+    return lds_frag<T, WUNITS>(w_lds, 32 * mt + r, 2 * c + hh);
+  } else {
+    const T* wp = mt < 16 ? wsrc[mt >> 2] + (size_t)((mt & 3) * 32 + r) * CZ : wsrc[4] + (size_t)(r < NH ? r : 0) * CZ;
+    return gld8<T>(wp + 16 * c + 8 * hh);
+  }
+}
+
+// NT output tiles mt0 .. mt0+NT-1 of one wave's 32 tokens.  SWAP puts the tokens
+// on the A side (rows), which yields the transposed tile (v^T).
+template <typename T, int WUNITS, int NT, bool SWAP>
+__device__ __forceinline__ void proj_tiles(const u32x4* w_lds, const T* const* wsrc, int mt0, int r, int hh,
+                                           const typename El<T>::frag* xf, f32x16* acc) {
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x16{};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    typename El<T>::frag wf[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) wf[j] = proj_wfrag<T, WUNITS>(w_lds, wsrc, mt0 + j, r, hh, c);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = SWAP ? mma(xf[c], wf[j], acc[j]) : mma(wf[j], xf[c], acc[j]);
+  }
+}
+
 template <typename T>
-__global__ void __launch_bounds__(NTHREADS) tri_project(ProjectArgs a) {
-  constexpr bool W_IN_LDS = sizeof(T) == 2;
+__device__ __forceinline__ void store16(T* p, const float* o) {
+  gst8<T>(p, to_frag<T>(o));
+  gst8<T>(p + 8, to_frag<T>(o + 8));
+}
+
+// What one launch writes: q, k, v^T, g and the pair bias; the four without the
+// bias (row blocks, whose bias comes from the caller); or the bias alone.
+enum { PROJ_ALL = 0, PROJ_NO_BIAS = 1, PROJ_BIAS_ONLY = 2 };
+
+template <typename T, int MODE>
+__global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArgs a) {
+  constexpr int WAVES = ProjCfg<T>::WAVES;
+  constexpr bool W_IN_LDS = ProjCfg<T>::W_IN_LDS;
+  constexpr int TP = 32 * WAVES;                   // positions per tile (divides P)
   constexpr int WUNITS = CZ * El<T>::bytes / 16;   // 16-B units per weight row
   constexpr int NW_ROWS = 17 * 32;
+  typedef typename El<T>::frag frag;
   __shared__ u32x4 w_lds[W_IN_LDS ? NW_ROWS * WUNITS : 1];
-  __shared__ float ln_lds[2 * CZ];
+  __shared__ __attribute__((aligned(64))) float par_lds[3 * CZ];  // gamma, beta, gate bias
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, lr = lane & 31;
   const T* wsrc[5] = {(const T*)a.w_q, (const T*)a.w_k, (const T*)a.w_v, (const T*)a.w_g, (const T*)a.w_b};
 
   if (W_IN_LDS) {
-    for (int idx = tid; idx < NW_ROWS * WUNITS; idx += NTHREADS) {
+    for (int idx = tid; idx < NW_ROWS * WUNITS; idx += 64 * WAVES) {
       int r = idx / WUNITS, u = idx % WUNITS, mt = r >> 5;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (mt < 4 * 4) v = reinterpret_cast<const u32x4*>(wsrc[mt >> 2] + (size_t)((mt & 3) * 32 + (r & 31)) * CZ)[u];
@@ -198,102 +259,120 @@ __global__ void __launch_bounds__(NTHREADS) tri_project(ProjectArgs a) {
       lds_put<WUNITS>(w_lds, r, u, v);
     }
   }
-  for (int c = tid; c < 2 * CZ; c += NTHREADS) ln_lds[c] = c < CZ ? a.ln_gamma[c] : a.ln_beta[c - CZ];
+  for (int c = tid; c < 3 * CZ; c += 64 * WAVES)
+    par_lds[c] = c < CZ ? a.ln_gamma[c] : c < 2 * CZ ? a.ln_beta[c - CZ] : (a.b_g ? a.b_g[c - 2 * CZ] : 0.f);
   __syncthreads();
 
-  const int pblocks = a.P / QB;
-  const long ntiles = (long)a.lines * pblocks;
-  const int mt0 = a.bias_only ? 16 : 0;
+  const int pblocks = a.P / TP;
+  const int ntiles = a.lines * pblocks;  // <= 65536 * 256
   const T* z = (const T*)a.z;
+  const int I1 = a.I - 1;
 
-  for (long tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int line = (int)(tile / pblocks);
-    const int pos0 = (int)(tile % pblocks) * QB + wave * 32;
+  // Raw token half of this lane for a tile.  Padding positions (>= I) repeat the
+  // last token: their results are finite and never read as real data.
+  auto load_z = [&](int t, frag* zp) {
+    const int line = t / pblocks;
+    const int pos = (t - line * pblocks) * TP + wave * 32 + rho(lr);
+    const int pc = pos < I1 ? pos : I1;
+    const T* zr = z + (size_t)line * a.z_line_stride + (size_t)pc * a.z_pos_stride + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) zp[c] = gld8<T>(zr + 16 * c);
+  };
+
+  frag zp[8];
+  int tile = blockIdx.x;
+  if (tile < ntiles) load_z(tile, zp);
+  for (; tile < ntiles; tile += gridDim.x) {
+    const int line = tile / pblocks;
+    const int pos0 = (tile - line * pblocks) * TP + wave * 32;
     const int pos = pos0 + rho(lr);
-    // ---- load the token half and normalise it
-    float x[64];
-    if (pos < a.I) {
-      const T* zp = z + (size_t)line * a.z_line_stride + (size_t)pos * a.z_pos_stride + 64 * hh;
+    // The weight rows are loop-invariant: hidden from the optimiser so that it
+    // does not hoist all 136 fragment reads (544 registers) out of the loop.
+    int wr = rho(lr);
+    asm volatile("" : "+v"(wr));
+    frag zc[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        typename El<T>::frag f = gld8<T>(zp + 8 * c);
-        frag_to_f32<T>(f, x + 8 * c);
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 64; ++t) x[t] = 0.f;
+    for (int c = 0; c < 8; ++c) zc[c] = zp[c];
+    {
+      const int nt = tile + (int)gridDim.x < ntiles ? tile + (int)gridDim.x : tile;  // the last tile reloads itself
+      load_z(nt, zp);
     }
+
+    // ---- LayerNorm: mean, then the centred second moment, then scale and shift
     float s = 0.f;
 #pragma unroll
-    for (int t = 0; t < 64; ++t) s += x[t];
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) s += (float)zc[c][t];
     const float mean = xhalf_sum(s) * (1.0f / CZ);
     float v2 = 0.f;
 #pragma unroll
-    for (int t = 0; t < 64; ++t) { x[t] -= mean; v2 += x[t] * x[t]; }
-    const float rstd = rsqrtf(xhalf_sum(v2) * (1.0f / CZ) + a.eps);
-    typename El<T>::frag xf[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float t8[8];
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        int ch = 64 * hh + 8 * c + t;
-        t8[t] = x[8 * c + t] * rstd * ln_lds[ch] + ln_lds[CZ + ch];
+        const float d = (float)zc[c][t] - mean;
+        v2 += d * d;
       }
+    const float rstd = rsqrtf(xhalf_sum(v2) * (1.0f / CZ) + a.eps);
+    frag xf[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const f32x8 gm = *reinterpret_cast<const f32x8*>(par_lds + 16 * c + 8 * hh);
+      const f32x8 bt = *reinterpret_cast<const f32x8*>(par_lds + CZ + 16 * c + 8 * hh);
+      float t8[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) t8[t] = ((float)zc[c][t] - mean) * rstd * gm[t] + bt[t];
       xf[c] = to_frag<T>(t8);
     }
 
-    // ---- 17 output tiles
-    for (int mt = mt0; mt < 17; ++mt) {
-      f32x16 acc = {};
-      const bool vt_tile = mt >= 8 && mt < 12;
-      const int wrow = 32 * mt + rho(lr);
+    f32x16 acc[4];
+    float o[16];
+    if (MODE != PROJ_BIAS_ONLY) {
+      // q (times log2(e)/sqrt(d)) and k: lane = token pos, channels 16*hh + i of head h
+      proj_tiles<T, WUNITS, 4, false>(w_lds, wsrc, 0, wr, hh, xf, acc);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        typename El<T>::frag wf;
-        if constexpr (W_IN_LDS) {
-          wf = lds_frag<T, WUNITS>(w_lds, wrow, 8 * hh + c);
-        } else {
-          const T* wp = mt < 16 ? wsrc[mt >> 2] + (size_t)((mt & 3) * 32 + rho(lr)) * CZ
-                                : wsrc[4] + (size_t)(rho(lr) < NH ? rho(lr) : 0) * CZ;
-          wf = gld8<T>(wp + 64 * hh + 8 * c);
-        }
-        acc = vt_tile ? mma(xf[c], wf, acc) : mma(wf, xf[c], acc);
+      for (int h = 0; h < NH; ++h) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[i] = acc[h][i] * (LOG2E * 0.17677669529663687f);
+        store16<T>((T*)a.q + (((size_t)line * NH + h) * a.P + pos) * HD + 16 * hh, o);
       }
-      const int head = mt & 3;
-      if (mt < 8 || (mt >= 12 && mt < 16)) {
-        // lane: token pos, channels 16*hh + i of head `head`
-        float o[16];
-        if (mt < 4) {
+      proj_tiles<T, WUNITS, 4, false>(w_lds, wsrc, 4, wr, hh, xf, acc);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[i] = acc[i] * (LOG2E * 0.17677669529663687f);  // log2(e)/sqrt(32)
-        } else if (mt < 8) {
+      for (int h = 0; h < NH; ++h) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[i] = acc[i];
-        } else {
+        for (int i = 0; i < 16; ++i) o[i] = acc[h][i];
+        store16<T>((T*)a.k + (((size_t)line * NH + h) * a.P + pos) * HD + 16 * hh, o);
+      }
+      // v^T: lane = channel rho(lr) of head h, tokens pos0 + 16*hh + i
+      proj_tiles<T, WUNITS, 4, true>(w_lds, wsrc, 8, wr, hh, xf, acc);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float bg = a.b_g ? a.b_g[head * HD + 16 * hh + i] : 0.f;
-            o[i] = sigmoidf_(acc[i] + bg);
-          }
-        }
-        T* dst = (T*)(mt < 4 ? a.q : mt < 8 ? a.k : a.g);
-        T* p = dst + (((size_t)line * NH + head) * a.P + pos) * HD + 16 * hh;
-        gst8<T>(p, to_frag<T>(o));
-        gst8<T>(p + 8, to_frag<T>(o + 8));
-      } else if (vt_tile) {
-        // lane: channel e = rho(lr) of head, tokens pos0 + 16*hh + i
-        float o[16];
+      for (int h = 0; h < NH; ++h) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[i] = acc[i];
-        T* p = (T*)a.vt + (((size_t)line * NH + head) * HD + rho(lr)) * a.P + pos0 + 16 * hh;
-        gst8<T>(p, to_frag<T>(o));
-        gst8<T>(p + 8, to_frag<T>(o + 8));
-      } else if (a.bias != nullptr && hh == 0 && pos < a.I) {
-        // bias tile: lanes of the lower half hold channels 0..15; heads are 0..3
+        for (int i = 0; i < 16; ++i) o[i] = acc[h][i];
+        store16<T>((T*)a.vt + (((size_t)line * NH + h) * HD + rho(lr)) * a.P + pos0 + 16 * hh, o);
+      }
+      // gate after the sigmoid
+      proj_tiles<T, WUNITS, 4, false>(w_lds, wsrc, 12, wr, hh, xf, acc);
 #pragma unroll
-        for (int h = 0; h < NH; ++h)
-          a.bias[((size_t)h * a.I + a.bias_row0 + line) * a.I + pos] = acc[h];
+      for (int h = 0; h < NH; ++h) {
+        const f32x16 bg = *reinterpret_cast<const f32x16*>(par_lds + 2 * CZ + h * HD + 16 * hh);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[i] = sigmoidf_(acc[h][i] + bg[i]);
+        store16<T>((T*)a.g + (((size_t)line * NH + h) * a.P + pos) * HD + 16 * hh, o);
+      }
+    }
+    if (MODE != PROJ_NO_BIAS) {
+      // pair bias: rows 0..3 of the tile, in the lanes of the lower half (i = head).
+      // One buffer resource per head spans exactly this line's I entries, so
+      // the upper half (pushed past the end) and positions >= I are dropped by
+      // the hardware range check instead of a branch.
+      proj_tiles<T, WUNITS, 1, false>(w_lds, wsrc, 16, wr, hh, xf, acc);
+      const int boff = (pos + hh * a.I) * 4;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        float* row = a.bias + ((size_t)h * a.I + a.bias_row0 + line) * a.I;
+        __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, a.I * 4, BUF_DWORD3);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[0][h]), rs, boff, 0, 0);
       }
     }
   }
@@ -694,15 +773,24 @@ static int cu_count() {
 }
 
 hipError_t launch_project(const ProjectArgs& a, int dtype, hipStream_t stream) {
-  const long ntiles = (long)a.lines * (a.P / QB);
-  long grid = cu_count();
-  if (dtype == 2) grid *= 4;  // fp32 keeps its weights in global memory: more workgroups fit
+  // Persistent: bf16 holds its weights in LDS (one workgroup per CU); fp32 reads
+  // them through the caches, so several workgroups share a CU.
+  const int waves = dtype == 1 ? ProjCfg<__bf16>::WAVES : ProjCfg<float>::WAVES;
+  const long ntiles = (long)a.lines * (a.P / (32 * waves));
+  long grid = dtype == 1 ? cu_count() : 4L * cu_count();
   if (grid > ntiles) grid = ntiles;
   if (grid < 1) grid = 1;
-  if (dtype == 1)
-    hipLaunchKernelGGL(tri_project<__bf16>, dim3((unsigned)grid), dim3(NTHREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(tri_project<float>, dim3((unsigned)grid), dim3(NTHREADS), 0, stream, a);
+  const int mode = a.bias_only ? PROJ_BIAS_ONLY : a.bias != nullptr ? PROJ_ALL : PROJ_NO_BIAS;
+  const dim3 g((unsigned)grid), b(64 * waves);
+  if (dtype == 1) {
+    if (mode == PROJ_ALL) hipLaunchKernelGGL((tri_project<__bf16, PROJ_ALL>), g, b, 0, stream, a);
+    else if (mode == PROJ_NO_BIAS) hipLaunchKernelGGL((tri_project<__bf16, PROJ_NO_BIAS>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((tri_project<__bf16, PROJ_BIAS_ONLY>), g, b, 0, stream, a);
+  } else {
+    if (mode == PROJ_ALL) hipLaunchKernelGGL((tri_project<float, PROJ_ALL>), g, b, 0, stream, a);
+    else if (mode == PROJ_NO_BIAS) hipLaunchKernelGGL((tri_project<float, PROJ_NO_BIAS>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((tri_project<float, PROJ_BIAS_ONLY>), g, b, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
