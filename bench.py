@@ -44,13 +44,13 @@ def flops(I, rows, with_bias):
 
 
 def k1_bytes(I, rows, es, with_bias):
-    """Algorithmic HBM bytes of K1: read Z, write q, k, v^T, g (and the fp32 bias)."""
+    """Algorithmic HBM bytes of K1: read Z, write q, k, v^T, g (and the fp32 pair bias)."""
     return rows * I * 128 * es * 5 + (4 * I * I * 4 if with_bias else 0)
 
 
 def k2_bytes(I, rows, es):
-    """Algorithmic HBM bytes of K2: read q, k, v^T, g and the fp32 bias once, write out."""
-    return rows * I * 128 * es * 5 + 4 * I * I * 4
+    """Algorithmic HBM bytes of K2: read q, k, v^T, g and the packed bias (fp16 / fp32) once, write out."""
+    return rows * I * 128 * es * 5 + 4 * I * I * es
 
 
 def kernel_sha():
@@ -69,51 +69,170 @@ def read_traffic(workload):
     return float(m.group(1))
 
 
-def cpu_baseline(wl, z_host, w_host, target_s=12.0):
-    """The float64 oracle on a bounded sample of rows of the workload, over a process pool."""
+def cpu_baseline(wl, z_host, w_host, target_s=20.0):
+    """The float64 oracle on a bounded sample of rows of the workload, over a process pool.
+
+    The whole pair bias is computed first (it is shared by every row), then rows
+    spread evenly over the line are run one per worker and process; a first round
+    of one row per worker sizes the remaining rounds to about `target_s` in total.
+    """
     import multiprocessing as mp
 
     import numpy as np
+    from threadpoolctl import threadpool_limits
+
     from oracle import ref
     from protein_pair_representation_amd import inputs
 
-    workers = max(1, min(16, os.cpu_count() or 1))
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
     I = wl.I
     p = ref.params(inputs.weights_f64(w_host), 4, 32)
     z64 = inputs.to_f64(z_host)
     t0 = time.perf_counter()
-    bias = ref.pair_bias(z64, p)                    # whole bias, single process
+    with threadpool_limits(limits=workers):
+        bias = ref.pair_bias(z64, p)
     t_bias = time.perf_counter() - t0
     f_bias = 2.0 * I * I * 128 * 4
-    # calibrate one row, then size the sample to about target_s of wall time
-    t0 = time.perf_counter()
-    ref.triangle_attn_rows(z64[:1], bias, p)
-    t_row = time.perf_counter() - t0
-    n_rows = int(max(workers, min(I, workers * max(1, round((target_s - t_bias) / max(t_row, 1e-3) / 1.0)))))
-    n_rows = min(n_rows, I)
-    rows = np.linspace(0, I - 1, n_rows).astype(int)
-    chunks = [rows[i::workers] for i in range(workers)]
+    order = np.argsort((np.arange(I) * 0.6180339887498949) % 1.0, kind="stable")  # spread-out rows
     ctx = mp.get_context("fork")
+    done = 0
     t0 = time.perf_counter()
     with ctx.Pool(workers, initializer=_limit_blas) as pool:
-        pool.starmap(_oracle_rows, [(z64[c], bias, p) for c in chunks if len(c)])
+        def run_round(k):
+            rows = order[k * workers:(k + 1) * workers]
+            pool.starmap(_oracle_rows, [(z64[r:r + 1], bias, p) for r in rows])
+            return len(rows)
+        done += run_round(0)
+        t_round = time.perf_counter() - t0
+        rounds = int(max(0, min((I - done) // workers, (target_s - t_bias - t_round) // max(t_round, 1e-3))))
+        for k in range(1, rounds + 1):
+            done += run_round(k)
     t_rows = time.perf_counter() - t0
-    proj, attn, out = flops(I, n_rows, False)
+    proj, attn, out = flops(I, done, False)
     total_f = f_bias + proj + attn + out
     total_t = t_bias + t_rows
-    return {"value": total_f / total_t / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
-            "sample": f"{wl.name}: whole pair bias (1 process) + starting-node rows {n_rows} of {I} "
-                      f"({workers} processes, 1 BLAS thread each), float64 NumPy; {total_t:.1f} s"}
+    return {"value": round(total_f / total_t / 1e12, 5), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"{wl.name}: the whole pair bias ({workers} BLAS threads) + starting-node rows {done} of {I} "
+                      f"({workers} processes, 1 BLAS thread each), float64 NumPy; {total_t:.1f} s wall"}
 
 
 def _limit_blas():
-    os.environ["OMP_NUM_THREADS"] = "1"
-    os.environ["OPENBLAS_NUM_THREADS"] = "1"
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
 
 
 def _oracle_rows(z_rows, bias, p):
     from oracle import ref
     return ref.triangle_attn_rows(z_rows, bias, p).shape
+
+
+def _counter_csv(d):
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {d}, found {files}")
+    return files[0]
+
+
+def _per_dispatch(path, counter):
+    """{kernel name: [per-dispatch value]} for one counter (values summed over a dispatch's rows)."""
+    import csv
+    import collections
+    acc = collections.defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        acc[r["Dispatch_Id"]] += float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    out = collections.defaultdict(list)
+    for k, v in acc.items():
+        out[names[k]].append(v)
+    return out
+
+
+def _short(name):
+    for key in ("tri_attend", "tri_project", "tri_pack_bias", "copyBuffer"):
+        if key in name:
+            return key
+    return name[:60]
+
+
+def summarize_pmc(run_dir, workload, copy_mib):
+    """Write the HBM-traffic summary of tri_attend / tri_project from four rocprofv3 --pmc runs.
+
+    run_dir holds pmc_fetch/ and pmc_write/ (bench.py under FETCH_SIZE and WRITE_SIZE)
+    and pmc_copy_fetch/, pmc_copy_write/ (bench.py --copy-calibration under the same
+    counters).  Each counter is scaled by (bytes the copy kernel moves) / (what the
+    counter reads for it).
+    """
+    copy_bytes = copy_mib << 20
+    cf = _per_dispatch(_counter_csv(os.path.join(run_dir, "pmc_copy_fetch")), "FETCH_SIZE")
+    cw = _per_dispatch(_counter_csv(os.path.join(run_dir, "pmc_copy_write")), "WRITE_SIZE")
+    copy_f = [v for k, v in cf.items() if "copyBuffer" in k][0]
+    copy_w = [v for k, v in cw.items() if "copyBuffer" in k][0]
+    f_scale = copy_bytes / (sum(copy_f) / len(copy_f) * 1024)
+    w_scale = copy_bytes / (sum(copy_w) / len(copy_w) * 1024)
+    kf = _per_dispatch(_counter_csv(os.path.join(run_dir, "pmc_fetch")), "FETCH_SIZE")
+    kw = _per_dispatch(_counter_csv(os.path.join(run_dir, "pmc_write")), "WRITE_SIZE")
+    lines = []
+    per = {}
+    for name in sorted(set(kf) | set(kw)):
+        sh = _short(name)
+        if not sh.startswith("tri_"):
+            continue
+        f = kf.get(name, [0.0])
+        w = kw.get(name, [0.0])
+        fb = sum(f) / len(f) * 1024 * f_scale
+        wb = sum(w) / len(w) * 1024 * w_scale
+        per[sh] = fb + wb
+        lines.append(f"{sh:14s} dispatches {len(f):3d}  FETCH_SIZE {sum(f) / len(f):12.1f} KiB  WRITE_SIZE "
+                     f"{sum(w) / len(w):12.1f} KiB  -> HBM read {fb / 1e6:9.2f} MB  write {wb / 1e6:9.2f} MB")
+    wl_path = os.path.join(PROFILE_DIR, f"tri_attend_{workload}_pmc.txt")
+    sha = kernel_sha()
+    cmd_b = f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline"
+    cmd_c = f"python3 $R/bench.py --copy-calibration {copy_mib}"
+    txt = [f"# HBM traffic per dispatch, workload {workload}, gfx950 (MI355X)",
+           "# commands (R = repository root, O = output directory, run from /tmp):",
+           f"#   timeout -s KILL 100 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $O/pmc_fetch -o f -- {cmd_b}",
+           f"#   timeout -s KILL 100 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $O/pmc_write -o w -- {cmd_b}",
+           f"#   timeout -s KILL 100 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $O/pmc_copy_fetch -o cf -- {cmd_c}",
+           f"#   timeout -s KILL 100 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $O/pmc_copy_write -o cw -- {cmd_c}",
+           f"#   python3 bench.py --summarize-pmc $O --workload {workload}",
+           f"# calibration: a {copy_mib} MiB device copy reads FETCH_SIZE {sum(copy_f) / len(copy_f):.1f} KiB and "
+           f"WRITE_SIZE {sum(copy_w) / len(copy_w):.1f} KiB;",
+           f"#   scale factors FETCH x{f_scale:.4f}, WRITE x{w_scale:.4f}",
+           *lines,
+           f"traffic_bytes_per_launch={per.get('tri_attend', 0.0):.6e} kernel_sha={sha}",
+           f"tri_project_traffic_bytes_per_launch={per.get('tri_project', 0.0):.6e} kernel_sha={sha}"]
+    open(wl_path, "w").write("\n".join(txt) + "\n")
+    print("\n".join(txt))
+
+
+def summarize_trace(run_dir, workload, steps, warmup):
+    """Write the per-kernel duration summary from a rocprofv3 --kernel-trace --stats csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one kernel_stats.csv under {run_dir}, found {files}")
+    rows = list(csv.DictReader(open(files[0])))
+    out = [f"# rocprofv3 kernel statistics, workload {workload}, gfx950 (MI355X)",
+           "# command (R = repository root, O = output directory, run from /tmp):",
+           f"#   timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d $O/kt -o kt -- "
+           f"python3 $R/bench.py --workload {workload} --steps {steps} --warmup {warmup} --no-cpu-baseline",
+           f"#   python3 bench.py --summarize-trace $O/kt --workload {workload} --steps {steps} --warmup {warmup}",
+           f"# kernel_sha={kernel_sha()}",
+           f"{'kernel':16s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for r in rows:
+        sh = _short(r["Name"])
+        if not sh.startswith("tri_"):
+            continue
+        out.append(f"{sh:16s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} {float(r['MinNs']) / 1e3:10.1f} "
+                   f"{float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}")
+    path = os.path.join(PROFILE_DIR, f"kernels_{workload}_trace.txt")
+    open(path, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
 
 
 def main():
@@ -125,10 +244,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="write the HBM-traffic summary under profiles/ from rocprofv3 --pmc runs in DIR, and exit")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write the kernel-duration summary under profiles/ from a rocprofv3 --stats run, and exit")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy (--summarize-pmc)")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.workload, args.copy_mib)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload, args.steps, args.warmup)
+        return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the sharded path is described, not built.", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
+              "row sharding over several GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -229,7 +359,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(k2_tflops / peak, 4),
                      "traffic": traffic, "algorithmic_bytes": k2_bytes(I, R, es),
                      "flops_per_launch": k2_flops, "avg_launch_ms": round(k2_ms, 4)},
-        "kernels": {"tri_project": {"avg_launch_ms": round(k1_ms, 4), "algorithmic_bytes": k1b,
+        "kernels": {"project_stage (tri_project + tri_pack_bias)": {"avg_ms": round(k1_ms, 4), "algorithmic_bytes": k1b,
                                     "GB/s": round(k1b / (k1_ms * 1e-3) / 1e9, 1),
                                     "frac_hbm": round(k1b / (k1_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
                     "tri_attend": {"avg_launch_ms": round(k2_ms, 4), "TFLOP/s": round(k2_tflops, 2)}},

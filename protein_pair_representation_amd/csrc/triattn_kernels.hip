@@ -509,7 +509,8 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
   constexpr int QBW = 32 * WAVES;                  // queries per workgroup
   __shared__ u32x4 kv_lds[2][STAGE_UNITS];         // [buffer][row][K tile | V^T tile]
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, lr = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, lr = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar addressing
   const int I = a.I, P = a.P;
   const int n_lg = (a.lines + ROWS - 1) / ROWS;
   int lg, qb;
@@ -522,21 +523,24 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
   auto line_of = [&](int r) { return line0 + r < a.lines ? line0 + r : a.lines - 1; };
   const size_t tok_line = (size_t)NH * P * HD;     // q, k, g, o and v^T elements per line
 
-  // staging: thread tid moves LDT units; slot s covers unit tid + s*NT of the stage
-  int g_off[LDT], l_off[LDT];
-  const T* g_base[LDT];
+  // staging: thread tid moves LDT units; slot s covers unit (s % SPR)*NT + tid of
+  // row s / SPR, a K unit or a V^T unit for every thread alike (KTILE_UNITS is a
+  // multiple of NT), so each load is a scalar base plus a fixed per-lane offset.
+  static_assert(KTILE_UNITS % NT == 0 && VTILE_UNITS % NT == 0, "staging slots must not straddle K and V^T");
+  constexpr int SPR = ROW_UNITS / NT;              // slots per row
+  constexpr int SPK = KTILE_UNITS / NT;            // of which K slots
+  uint32_t g_off[LDT];                             // per-lane byte offset inside the tile
+  int l_off[LDT];
 #pragma unroll
   for (int s = 0; s < LDT; ++s) {
-    const int idx = tid + s * NT, r = idx / ROW_UNITS, w = idx - r * ROW_UNITS;
-    if (w < KTILE_UNITS) {
+    const int r = s / SPR, w = (s % SPR) * NT + tid;
+    if ((s % SPR) < SPK) {
       const int row = w / KU, u = w % KU;
-      g_base[s] = (const T*)a.k + line_of(r) * tok_line;
-      g_off[s] = row * HD + u * EPU;               // + (h*P + kt*KT) * HD
+      g_off[s] = (uint32_t)(row * HD + u * EPU) * sizeof(T);
       l_off[s] = r * ROW_UNITS + row * KU + (u ^ swz<KU>(row));
     } else {
       const int ww = w - KTILE_UNITS, e = ww / VU, u = ww % VU;
-      g_base[s] = (const T*)a.vt + line_of(r) * tok_line;
-      g_off[s] = -(e * P + u * EPU) - 1;           // V marker: negative, decoded below
+      g_off[s] = (uint32_t)(e * P + u * EPU) * sizeof(T);
       l_off[s] = r * ROW_UNITS + KTILE_UNITS + e * VU + (u ^ swz<VU>(e));
     }
   }
@@ -544,10 +548,11 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
   auto load_tile = [&](int h, int kt) {
 #pragma unroll
     for (int s = 0; s < LDT; ++s) {
-      const int off = g_off[s];
-      const T* p = off >= 0 ? g_base[s] + ((size_t)h * P + kt * KT) * HD + off
-                            : g_base[s] + (size_t)h * HD * P + kt * KT + (-off - 1);
-      sreg[s] = *reinterpret_cast<const u32x4*>(p);
+      const int r = s / SPR;
+      const bool is_k = (s % SPR) < SPK;
+      const T* base = is_k ? (const T*)a.k + line_of(r) * tok_line + ((size_t)h * P + kt * KT) * HD
+                           : (const T*)a.vt + line_of(r) * tok_line + (size_t)h * HD * P + kt * KT;
+      sreg[s] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + g_off[s]);
     }
   };
   auto store_tile = [&](int buf) {
@@ -600,6 +605,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
   for (int h = 0; h < NH; ++h) {
     frag qf[ROWS][2], qm[ROWS];
     float m[ROWS], lsum[ROWS];
+    bool mact[ROWS];                               // wave-uniform: some lane of the row has m != 0
     f32x16 o[ROWS];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
@@ -608,6 +614,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       qf[r][1] = gld8<T>(qrow + 16);
       qm[r] = unit_frag<T>(0.f);
       m[r] = 0.f;
+      mact[r] = false;
       lsum[r] = 0.f;
       o[r] = zero;
     }
@@ -641,8 +648,10 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
         for (int st = 0; st < 2; ++st) sc[st] = mma(kf[st][0], qf[r][0], sbias[st]);
 #pragma unroll
         for (int st = 0; st < 2; ++st) sc[st] = mma(kf[st][1], qf[r][1], sc[st]);
+        if (mact[r]) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) sc[st] = mma(e0, qm[r], sc[st]);
+          for (int st = 0; st < 2; ++st) sc[st] = mma(e0, qm[r], sc[st]);
+        }
         if constexpr (FIRST) {
           // first tile: shift only if its maximum is far from 0
           const float mx = tile_max(sc);
@@ -654,6 +663,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
               for (int i = 0; i < 16; ++i) sc[st][i] -= mf;
             m[r] = mf;
             qm[r] = unit_frag<T>(hh == 0 ? -mf : 0.f);
+            mact[r] = true;
           }
         }
         frag pf[2][2];
@@ -662,6 +672,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
           float d;
           lt = rebase_tile<T>(sc, pf, m[r], o[r], lsum[r], d);
           qm[r] = unit_frag<T>(hh == 0 ? -m[r] : 0.f);
+          mact[r] = true;
         }
         lsum[r] += lt;
 #pragma unroll
