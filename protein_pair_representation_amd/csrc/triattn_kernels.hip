@@ -634,43 +634,52 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
 #pragma unroll
       for (int st = 0; st < 2; ++st) sbias[st] = mma(esel[1], bias_next[2 * st + 1], sbias[st]);
       load_bias(bias0 + hn * bias_head + ((size_t)ktn << 11), bias_next);
+      // scores of every row first, so that the exponentials of row r run on the
+      // VALU while the matrix core still works on row r+1 (and P.V of row r
+      // overlaps the exponentials of row r+1)
+      f32x16 sc[ROWS][2];
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
         const u32x4* kl = kv_lds[buf] + r * ROW_UNITS;
-        const u32x4* vl = kl + KTILE_UNITS;
         frag kf[2][2];
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int c = 0; c < 2; ++c) kf[st][c] = lds_frag<T, KU>(kl, 32 * st + rho(lr), 2 * c + hh);
-        f32x16 sc[2];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) sc[st] = mma(kf[st][0], qf[r][0], sbias[st]);
+        for (int st = 0; st < 2; ++st) sc[r][st] = mma(kf[st][0], qf[r][0], sbias[st]);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) sc[st] = mma(kf[st][1], qf[r][1], sc[st]);
+        for (int st = 0; st < 2; ++st) sc[r][st] = mma(kf[st][1], qf[r][1], sc[r][st]);
         if (mact[r]) {
 #pragma unroll
-          for (int st = 0; st < 2; ++st) sc[st] = mma(e0, qm[r], sc[st]);
+          for (int st = 0; st < 2; ++st) sc[r][st] = mma(e0, qm[r], sc[r][st]);
         }
-        if constexpr (FIRST) {
+      }
+      if constexpr (FIRST) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
           // first tile: shift only if its maximum is far from 0
-          const float mx = tile_max(sc);
+          const float mx = tile_max(sc[r]);
           const float mf = (mx > FIRST_LIMIT || mx < -FIRST_LIMIT) ? (float)(T)mx : 0.f;
           if (__builtin_amdgcn_ballot_w64(mf != 0.f) != 0) {
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-              for (int i = 0; i < 16; ++i) sc[st][i] -= mf;
+              for (int i = 0; i < 16; ++i) sc[r][st][i] -= mf;
             m[r] = mf;
             qm[r] = unit_frag<T>(hh == 0 ? -mf : 0.f);
             mact[r] = true;
           }
         }
+      }
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const u32x4* vl = kv_lds[buf] + r * ROW_UNITS + KTILE_UNITS;
         frag pf[2][2];
-        float lt = exp_tile<T>(sc, pf);
+        float lt = exp_tile<T>(sc[r], pf);
         if (__builtin_amdgcn_ballot_w64(!(lt <= SUM_LIMIT)) != 0) {
           float d;
-          lt = rebase_tile<T>(sc, pf, m[r], o[r], lsum[r], d);
+          lt = rebase_tile<T>(sc[r], pf, m[r], o[r], lsum[r], d);
           qm[r] = unit_frag<T>(hh == 0 ? -m[r] : 0.f);
           mact[r] = true;
         }
@@ -820,6 +829,9 @@ hipError_t launch_pack_bias(const float* src, void* dst, int I, int P, int dtype
 #ifndef TRIATTN_ROWS
 #define TRIATTN_ROWS 2
 #endif
+#ifndef TRIATTN_MINW
+#define TRIATTN_MINW 2  // waves per SIMD the bf16 attention kernel is compiled for
+#endif
 #ifndef TRIATTN_WAVES
 #define TRIATTN_WAVES 4
 #endif
@@ -831,7 +843,7 @@ hipError_t launch_attend(const AttendArgs& args, int dtype, hipStream_t stream) 
   const long nblk = (long)((a.lines + R - 1) / R) * a.nqb;
   // bf16: two waves per SIMD; fp32 (twice the fragment registers): one
   if (dtype == 1)
-    hipLaunchKernelGGL((tri_attend<__bf16, R, W, 2>), dim3((unsigned)nblk), dim3(W * 64), 0, stream, a);
+    hipLaunchKernelGGL((tri_attend<__bf16, R, W, TRIATTN_MINW>), dim3((unsigned)nblk), dim3(W * 64), 0, stream, a);
   else
     hipLaunchKernelGGL((tri_attend<float, R, W, 1>), dim3((unsigned)nblk), dim3(W * 64), 0, stream, a);
   return hipGetLastError();
