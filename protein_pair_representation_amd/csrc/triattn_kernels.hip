@@ -489,6 +489,46 @@ __device__ __forceinline__ void map_block(int bid, int n_lg, int nqb, int& lg, i
   }
 }
 
+// Output projection of a workgroup's rows: out^T[c][j] = sum_(h,e) W_o[c][h*32+e]
+// o^T[h*32+e][j] + b_o[c], from the gated head outputs in the workspace (this lane
+// reads back exactly the o values it wrote).
+template <typename T, int ROWS>
+__device__ __forceinline__ void out_projection(const AttendArgs& a, int line0, int j, int hh, int lr) {
+  typedef typename El<T>::frag frag;
+  const int I = a.I, P = a.P;
+  const size_t tok_line = (size_t)NH * P * HD;
+#pragma unroll 1
+  for (int r = 0; r < ROWS; ++r) {
+    if (line0 + r >= a.lines) break;
+    const int line = line0 + r;
+    const T* orow_ws = (const T*)a.o + (size_t)line * tok_line + (size_t)j * HD + 16 * hh;
+    T* orow = (T*)a.out + (a.out_transposed ? ((size_t)j * I + line) : ((size_t)line * I + j)) * CZ;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = a.b_o ? a.b_o[32 * ct + 16 * hh + i] : 0.f;
+      const T* wrow = (const T*)a.w_o + (size_t)(32 * ct + rho(lr)) * CZ + 16 * hh;
+#pragma unroll
+      for (int hd = 0; hd < NH; ++hd)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          frag wf = gld8<T>(wrow + 32 * hd + 8 * c);   // W_o is small and stays in L2
+          frag of = gld8<T>(orow_ws + (size_t)hd * P * HD + 8 * c);
+          acc = mma(wf, of, acc);
+        }
+      if (j < I) {
+        float ov[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ov[i] = acc[i];
+        T* p = orow + 32 * ct + 16 * hh;
+        gst8<T>(p, to_frag<T>(ov));
+        gst8<T>(p + 8, to_frag<T>(ov + 8));
+      }
+    }
+  }
+}
+
 // ROWS consecutive lines per workgroup (each wave works on all of them for its
 // 32 queries, so one bias tile serves ROWS rows), WAVES waves = 32*WAVES queries.
 template <typename T, int ROWS, int WAVES, int MIN_WAVES_PER_SIMD>
@@ -715,38 +755,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
     }
   }
 
-  // ---- output projection: out^T[c][j] = sum_(h,e) W_o[c][h*32+e] o^T[h*32+e][j] + b_o[c]
-  // (this lane reads back exactly the o values it wrote)
-#pragma unroll 1
-  for (int r = 0; r < ROWS; ++r) {
-    if (line0 + r >= a.lines) break;
-    const int line = line0 + r;
-    const T* orow_ws = (const T*)a.o + (size_t)line * tok_line + (size_t)j * HD + 16 * hh;
-    T* orow = (T*)a.out + (a.out_transposed ? ((size_t)j * I + line) : ((size_t)line * I + j)) * CZ;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      f32x16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = a.b_o ? a.b_o[32 * ct + 16 * hh + i] : 0.f;
-      const T* wrow = (const T*)a.w_o + (size_t)(32 * ct + rho(lr)) * CZ + 16 * hh;
-#pragma unroll
-      for (int hd = 0; hd < NH; ++hd)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          frag wf = gld8<T>(wrow + 32 * hd + 8 * c);   // W_o is small and stays in L2
-          frag of = gld8<T>(orow_ws + (size_t)hd * P * HD + 8 * c);
-          acc = mma(wf, of, acc);
-        }
-      if (j < I) {
-        float ov[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ov[i] = acc[i];
-        T* p = orow + 32 * ct + 16 * hh;
-        gst8<T>(p, to_frag<T>(ov));
-        gst8<T>(p + 8, to_frag<T>(ov + 8));
-      }
-    }
-  }
+  out_projection<T, ROWS>(a, line0, j, hh, lr);
 }
 
 // Bias pack: natural-log fp32 bias [H][I][I] (from K1 or the caller) into the
