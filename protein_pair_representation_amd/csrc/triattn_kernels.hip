@@ -226,10 +226,35 @@ __device__ __forceinline__ void proj_tiles(const u32x4* w_lds, const T* const* w
   }
 }
 
+// Store of one wave's 32 x 32 output block through a per-wave LDS buffer, so that
+// every global store instruction writes whole contiguous rows (1 KiB per
+// instruction for q/k/g, 64-B row segments for v^T) instead of 16-B pieces.
+// Lane (hh, lr) holds 16 values of block row `row` = rho(lr), columns 16*hh ..
+// 16*hh+15.  Block row r lives at gbase + r * gstride (elements), columns
+// contiguous.  The 16-B units of a row are XOR-swizzled by the row so that the
+// per-lane writes and the row-major reads both spread over the banks.
 template <typename T>
-__device__ __forceinline__ void store16(T* p, const float* o) {
-  gst8<T>(p, to_frag<T>(o));
-  gst8<T>(p + 8, to_frag<T>(o + 8));
+__device__ __forceinline__ int stage_swz(int r) { return ((r >> 1) & 1) | (((r >> 4) & 1) << 1); }
+
+template <typename T>
+__device__ __forceinline__ void stage_store(u32x4* buf, int row, int hh, int lane, const float* o, T* gbase,
+                                            size_t gstride) {
+  constexpr int RU = HD * (int)sizeof(T) / 16;     // 16-B units per block row
+  constexpr int LU = RU / 2;                       // units a lane holds
+  constexpr int EPU = 16 / (int)sizeof(T);
+  T vals[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) vals[i] = (T)o[i];
+  u32x4 units[LU];
+  __builtin_memcpy(units, vals, sizeof(units));
+#pragma unroll
+  for (int s = 0; s < LU; ++s) buf[row * RU + ((hh * LU + s) ^ stage_swz<T>(row))] = units[s];
+#pragma unroll
+  for (int i = 0; i < LU; ++i) {
+    const int U = 64 * i + lane, r = U / RU, uu = U % RU;
+    const u32x4 v = buf[r * RU + (uu ^ stage_swz<T>(r))];
+    *reinterpret_cast<u32x4*>(gbase + r * gstride + uu * EPU) = v;
+  }
 }
 
 // What one launch writes: q, k, v^T, g and the pair bias; the four without the
@@ -246,9 +271,12 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
   typedef typename El<T>::frag frag;
   __shared__ u32x4 w_lds[W_IN_LDS ? NW_ROWS * WUNITS : 1];
   __shared__ __attribute__((aligned(64))) float par_lds[3 * CZ];  // gamma, beta, gate bias
+  constexpr int SU = 32 * HD * (int)sizeof(T) / 16;                 // 16-B units of one output block
+  __shared__ u32x4 st_lds[WAVES * SU];                              // per-wave store staging
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, lr = lane & 31;
   const T* wsrc[5] = {(const T*)a.w_q, (const T*)a.w_k, (const T*)a.w_v, (const T*)a.w_g, (const T*)a.w_b};
+  u32x4* st_buf = st_lds + wave * SU;
 
   if (W_IN_LDS) {
     for (int idx = tid; idx < NW_ROWS * WUNITS; idx += 64 * WAVES) {
@@ -268,21 +296,33 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
   const T* z = (const T*)a.z;
   const int I1 = a.I - 1;
 
-  // Raw token half of this lane for a tile.  Padding positions (>= I) repeat the
-  // last token: their results are finite and never read as real data.
-  auto load_z = [&](int t, frag* zp) {
+  // Address of this lane's raw token half in a tile.  Padding positions (>= I)
+  // repeat the last token: their results are finite and never read as real data.
+  auto z_addr = [&](int t) {
+    t = t < ntiles ? t : ntiles - 1;
     const int line = t / pblocks;
     const int pos = (t - line * pblocks) * TP + wave * 32 + rho(lr);
     const int pc = pos < I1 ? pos : I1;
-    const T* zr = z + (size_t)line * a.z_line_stride + (size_t)pc * a.z_pos_stride + 8 * hh;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) zp[c] = gld8<T>(zr + 16 * c);
+    return z + (size_t)line * a.z_line_stride + (size_t)pc * a.z_pos_stride + 8 * hh;
   };
 
+  // The next tile's tokens are loaded one tile ahead, and the address of the
+  // tile after that is formed right after those loads are issued, ahead of the
+  // stores: a value live across the whole iteration cannot share registers with
+  // store data, so the loads never wait for earlier stores to release them.
+  typedef const __attribute__((address_space(1))) T* gptr;
   frag zp[8];
   int tile = blockIdx.x;
-  if (tile < ntiles) load_z(tile, zp);
-  for (; tile < ntiles; tile += gridDim.x) {
+  uint64_t zn = (uint64_t)z_addr(tile);
+  if (tile < ntiles) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) zp[c] = *reinterpret_cast<const __attribute__((address_space(1))) frag*>((gptr)zn + 16 * c);
+  }
+  zn = (uint64_t)z_addr(tile + gridDim.x);
+  // One tile.  The first one is peeled off the loop so that the loop is entered
+  // with as many stores in flight as its back edge carries: the wait for the
+  // prefetched tokens then never has to cover the previous tile's stores.
+  auto tile_body = [&](int tile) {
     const int line = tile / pblocks;
     const int pos0 = (tile - line * pblocks) * TP + wave * 32;
     const int pos = pos0 + rho(lr);
@@ -293,10 +333,11 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
     frag zc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) zc[c] = zp[c];
-    {
-      const int nt = tile + (int)gridDim.x < ntiles ? tile + (int)gridDim.x : tile;  // the last tile reloads itself
-      load_z(nt, zp);
-    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)  // (the last tile reloads itself)
+      zp[c] = *reinterpret_cast<const __attribute__((address_space(1))) frag*>((gptr)zn + 16 * c);
+    zn = (uint64_t)z_addr(tile + 2 * gridDim.x);
+    asm volatile("" : "+v"(zn));
 
     // ---- LayerNorm: mean, then the centred second moment, then scale and shift
     float s = 0.f;
@@ -334,14 +375,14 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
       for (int h = 0; h < NH; ++h) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[i] = acc[h][i] * (LOG2E * 0.17677669529663687f);
-        store16<T>((T*)a.q + (((size_t)line * NH + h) * a.P + pos) * HD + 16 * hh, o);
+        stage_store<T>(st_buf, rho(lr), hh, lane, o, (T*)a.q + (((size_t)line * NH + h) * a.P + pos0) * HD, HD);
       }
       proj_tiles<T, WUNITS, 4, false>(w_lds, wsrc, 4, wr, hh, xf, acc);
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[i] = acc[h][i];
-        store16<T>((T*)a.k + (((size_t)line * NH + h) * a.P + pos) * HD + 16 * hh, o);
+        stage_store<T>(st_buf, rho(lr), hh, lane, o, (T*)a.k + (((size_t)line * NH + h) * a.P + pos0) * HD, HD);
       }
       // v^T: lane = channel rho(lr) of head h, tokens pos0 + 16*hh + i
       proj_tiles<T, WUNITS, 4, true>(w_lds, wsrc, 8, wr, hh, xf, acc);
@@ -349,7 +390,7 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
       for (int h = 0; h < NH; ++h) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[i] = acc[h][i];
-        store16<T>((T*)a.vt + (((size_t)line * NH + h) * HD + rho(lr)) * a.P + pos0 + 16 * hh, o);
+        stage_store<T>(st_buf, rho(lr), hh, lane, o, (T*)a.vt + ((size_t)line * NH + h) * HD * a.P + pos0, a.P);
       }
       // gate after the sigmoid
       proj_tiles<T, WUNITS, 4, false>(w_lds, wsrc, 12, wr, hh, xf, acc);
@@ -358,7 +399,7 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
         const f32x16 bg = *reinterpret_cast<const f32x16*>(par_lds + 2 * CZ + h * HD + 16 * hh);
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[i] = sigmoidf_(acc[h][i] + bg[i]);
-        store16<T>((T*)a.g + (((size_t)line * NH + h) * a.P + pos) * HD + 16 * hh, o);
+        stage_store<T>(st_buf, rho(lr), hh, lane, o, (T*)a.g + (((size_t)line * NH + h) * a.P + pos0) * HD, HD);
       }
     }
     if (MODE != PROJ_NO_BIAS) {
@@ -375,7 +416,10 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[0][h]), rs, boff, 0, 0);
       }
     }
-  }
+  };
+  if (tile < ntiles) tile_body(tile);
+#pragma unroll 1
+  for (tile += gridDim.x; tile < ntiles; tile += gridDim.x) tile_body(tile);
 }
 
 // ================================================================ K2: fused attention
