@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TRIATTN_ABI_VERSION 1
+#define TRIATTN_ABI_VERSION 2
 
 /* Compute dtypes. */
 enum { TA_BF16 = 1, TA_F32 = 2 };
@@ -183,12 +183,43 @@ int triangle_attn_project(const ta_problem* prob, int variant, const ta_weights*
 
 /* Stage 2 alone: fused attention + gate + output projection from a workspace
  * filled by triangle_attn_project with the same problem and variant.  `bias`
- * is required for TA_ROWS (natural-log units, [H][I][I]; it is first copied,
- * scaled by log2(e), into the workspace) and must be NULL otherwise (the
- * workspace already holds it). */
+ * is required for TA_ROWS (natural-log units, [H][I][I]; it is first packed,
+ * shifted per query and scaled by log2(e), into the workspace) and must be NULL
+ * otherwise (the workspace already holds it).  Writes the workspace's `o`
+ * region (and, for TA_ROWS, its packed bias). */
 int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* w,
-                         const float* bias, void* out, const void* ws, size_t ws_bytes,
+                         const float* bias, void* out, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* Key-block stage: the per-device step of attention whose keys and values
+ * arrive in blocks (the 2D grid sharding of the Design-CP summary,
+ * Methodology section 1, passes K/V blocks around; the softmax over keys is
+ * then merged from partial states, as ring attention computes scores on the
+ * fly).  For every (line, head, query) of the workspace a state is carried in
+ * fp32: the shift m (base-2 units), the sum l of exp2(score - m) and the
+ * unnormalised output O = sum exp2(score - m) v.  A call folds keys
+ * [key0, key0 + nkeys) into it.  Blocks may come in any order; once every key
+ * has been folded exactly once, triangle_attn_attend_finalize gives what
+ * triangle_attn_attend gives (up to rounding).
+ *   key0    a multiple of 64, 0 <= key0 < I
+ *   nkeys   >= 1, key0 + nkeys <= I, a multiple of 64 unless key0 + nkeys == I
+ *   first   non-zero: the state is started afresh (its content is ignored); for
+ *           TA_ROWS the caller's fp32 bias [H][I][I] is packed into the
+ *           workspace by this call (bias required).  Zero: the state carries the
+ *           earlier blocks, bias is ignored (may be NULL)
+ *   state   fp32, triangle_attn_state_bytes() bytes: O [L][H][P][d], then at the
+ *           next 256-byte boundary (m, l) [L][H][P][2] (L, P as in the layout)
+ *   ws      filled by triangle_attn_project with the same problem and variant */
+int triangle_attn_state_bytes(const ta_problem* prob, int variant, size_t* bytes);
+int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_weights* w,
+                               const float* bias, int32_t key0, int32_t nkeys, int32_t first,
+                               float* state, void* ws, size_t ws_bytes, void* stream);
+
+/* Finish a key-block accumulation: o = O / l, sigmoid gate, output projection,
+ * out as in triangle_attn_attend.  Writes the workspace's `o` region. */
+int triangle_attn_attend_finalize(const ta_problem* prob, int variant, const ta_weights* w,
+                                  const float* state, void* out, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 #ifdef __cplusplus
 }

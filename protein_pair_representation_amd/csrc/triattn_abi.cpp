@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kCz = 128, kHeads = 4, kHeadDim = 32, kPosAlign = 256, kMaxI = 65536;
+constexpr int kCz = 128, kHeads = 4, kHeadDim = 32, kPosAlign = 256, kMaxI = 65536, kKeyTile = 64;
 
 size_t esize(int dtype) { return dtype == TA_BF16 ? 2 : 4; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -126,7 +126,7 @@ triattn::ProjectArgs project_args(const ta_problem* p, int variant, const ta_wei
 }
 
 triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weights* w, const float* bias,
-                                void* out, const void* ws, const ta_ws_layout& l) {
+                                void* out, void* ws, const ta_ws_layout& l) {
   triattn::AttendArgs a;
   memset(&a, 0, sizeof(a));
   const char* base = (const char*)ws;
@@ -144,7 +144,15 @@ triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weigh
   a.P = l.positions;
   a.lines = l.lines;
   a.out_transposed = variant == TA_END ? 1 : 0;
+  a.kt0 = 0;
+  a.nbt = (p->I + kKeyTile - 1) / kKeyTile;  // every key
   return a;
+}
+
+// State of the key-block stage: O [L][H][P][d] fp32, then (m, l) [L][H][P][2] fp32.
+void state_sizes(const ta_ws_layout& l, size_t* o_bytes, size_t* total) {
+  *o_bytes = align256((size_t)l.lines * kHeads * l.positions * kHeadDim * sizeof(float));
+  *total = *o_bytes + align256((size_t)l.lines * kHeads * l.positions * 2 * sizeof(float));
 }
 
 int enqueue(hipError_t e) { return e == hipSuccess ? TA_OK : TA_ERR_HIP; }
@@ -273,7 +281,7 @@ int triangle_attn_project(const ta_problem* prob, int variant, const ta_weights*
 }
 
 int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* w, const float* bias, void* out,
-                         const void* ws, size_t ws_bytes, void* stream) {
+                         void* ws, size_t ws_bytes, void* stream) {
   int rc = check_problem(prob, variant);
   if (rc) return rc;
   if ((rc = check_weights(w))) return rc;
@@ -288,8 +296,76 @@ int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* 
   const Span bspan = {bias, bias ? (size_t)kHeads * prob->I * prob->I * sizeof(float) : 0};
   if ((rc = check_out_alias(prob, w, {out, tok_bytes}, {nullptr, 0}, {ws, l.total}, bspan))) return rc;
   (void)hipGetLastError();
-  if (variant == TA_ROWS && (rc = pack_bias(prob, variant, bias, (void*)ws, l, (hipStream_t)stream))) return rc;
+  if (variant == TA_ROWS && (rc = pack_bias(prob, variant, bias, ws, l, (hipStream_t)stream))) return rc;
   triattn::AttendArgs a = attend_args(prob, variant, w, bias, out, ws, l);
+  return enqueue(triattn::launch_attend(a, prob->dtype, (hipStream_t)stream));
+}
+
+int triangle_attn_state_bytes(const ta_problem* prob, int variant, size_t* bytes) {
+  int rc = check_problem(prob, variant);
+  if (rc) return rc;
+  if (bytes == nullptr) return TA_ERR_NULL_PTR;
+  ta_ws_layout l;
+  layout_of(prob, variant, &l);
+  size_t ob;
+  state_sizes(l, &ob, bytes);
+  return TA_OK;
+}
+
+int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_weights* w, const float* bias,
+                               int32_t key0, int32_t nkeys, int32_t first, float* state, void* ws,
+                               size_t ws_bytes, void* stream) {
+  int rc = check_problem(prob, variant);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (state == nullptr || ws == nullptr) return TA_ERR_NULL_PTR;
+  const bool pack = variant == TA_ROWS && first != 0;
+  if (pack && bias == nullptr) return TA_ERR_NULL_PTR;
+  if (!aligned16(state) || !aligned16(ws) || (pack && !aligned16(bias))) return TA_ERR_MISALIGNED;
+  const int I = prob->I;
+  if (key0 < 0 || key0 >= I || key0 % kKeyTile != 0 || nkeys < 1 || nkeys > I - key0 ||
+      (nkeys % kKeyTile != 0 && key0 + nkeys != I))
+    return TA_ERR_BAD_SHAPE;
+  ta_ws_layout l;
+  layout_of(prob, variant, &l);
+  if (ws_bytes < l.total) return TA_ERR_WORKSPACE_TOO_SMALL;
+  size_t ob, sb;
+  state_sizes(l, &ob, &sb);
+  const Span bspan = {pack ? bias : nullptr, pack ? (size_t)kHeads * I * I * sizeof(float) : 0};
+  if ((rc = check_out_alias(prob, w, {state, sb}, {nullptr, 0}, {ws, l.total}, bspan))) return rc;
+  (void)hipGetLastError();
+  if (pack && (rc = pack_bias(prob, variant, bias, ws, l, (hipStream_t)stream))) return rc;
+  triattn::AttendArgs a = attend_args(prob, variant, w, nullptr, nullptr, ws, l);
+  a.kt0 = key0 / kKeyTile;
+  a.nbt = (nkeys + kKeyTile - 1) / kKeyTile;
+  a.state_o = state;
+  a.state_ml = (float*)((char*)state + ob);
+  a.state_in = first ? 0 : 1;
+  a.state_out = 1;
+  return enqueue(triattn::launch_attend(a, prob->dtype, (hipStream_t)stream));
+}
+
+int triangle_attn_attend_finalize(const ta_problem* prob, int variant, const ta_weights* w, const float* state,
+                                  void* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_problem(prob, variant);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (state == nullptr || out == nullptr || ws == nullptr) return TA_ERR_NULL_PTR;
+  if (!aligned16(state) || !aligned16(out) || !aligned16(ws)) return TA_ERR_MISALIGNED;
+  ta_ws_layout l;
+  layout_of(prob, variant, &l);
+  if (ws_bytes < l.total) return TA_ERR_WORKSPACE_TOO_SMALL;
+  size_t ob, sb;
+  state_sizes(l, &ob, &sb);
+  const size_t tok_bytes = (size_t)prob->rows * prob->I * kCz * esize(prob->dtype);
+  if ((rc = check_out_alias(prob, w, {out, tok_bytes}, {nullptr, 0}, {ws, l.total}, {state, sb}))) return rc;
+  (void)hipGetLastError();
+  triattn::AttendArgs a = attend_args(prob, variant, w, nullptr, out, ws, l);
+  a.nbt = 0;  // no keys: gate and output projection of the carried state
+  a.state_o = (float*)state;
+  a.state_ml = (float*)((const char*)state + ob);
+  a.state_in = 1;
+  a.state_out = 0;
   return enqueue(triattn::launch_attend(a, prob->dtype, (hipStream_t)stream));
 }
 

@@ -34,6 +34,13 @@ struct AttendArgs {
   int I, P, lines;
   int nqb;                // query blocks (set by launch_attend from the block width)
   int out_transposed;     // 1: out[j][line], 0: out[line][j]
+  // key range: tiles kt0 .. kt0+nbt-1 of 64 keys (the whole row: 0, ceil(I/64))
+  int kt0, nbt;
+  // carried softmax state (key-block mode): O [lines][H][P][d] and (m, l) [lines][H][P][2], fp32
+  float* state_o;
+  float* state_ml;
+  int state_in;           // 1: start every head from the state instead of empty
+  int state_out;          // 1: store the state at the end of every head (no gate, no output projection)
 };
 
 hipError_t launch_project(const ProjectArgs& a, int dtype, hipStream_t stream);

@@ -601,7 +601,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
   map_block(blockIdx.x, n_lg, a.nqb, lg, qb);
   const int line0 = lg * ROWS;
   const int j = qb * QBW + wave * 32 + lr;         // this lane's query
-  const int nkt = (I + KT - 1) / KT;
+  const int kt0 = a.kt0, nbt = a.nbt;             // key tiles kt0 .. kt0+nbt-1
 
   // line of row r (rows past the last line repeat it and are never stored)
   auto line_of = [&](int r) { return line0 + r < a.lines ? line0 + r : a.lines - 1; };
@@ -670,18 +670,19 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
   const BT* bias0 = (const BT*)a.bias + ((size_t)(jb < jb_last ? jb : jb_last) * (P >> 6) << 11);
   const size_t bias_head = (size_t)P * P;        // elements per head; key tile stride 2048
 
-  // global key tile g = h * nkt + kt (past the end: the last tile again, unused)
-  const int ntiles = NH * nkt;
+  // step g = h * nbt + kt walks the key tiles kt0 + kt of every head (past the
+  // end: the last tile again, unused)
+  const int ntiles = NH * nbt;
   auto split = [&](int g, int& h, int& kt) {
     g = g < ntiles ? g : ntiles - 1;
-    h = g / nkt;
-    kt = g - h * nkt;
+    h = g / nbt;
+    kt = g - h * nbt;
   };
   bfrag bias_next[4];
-  {
-    load_tile(0, 0);
+  if (nbt > 0) {
+    load_tile(0, kt0);
     store_tile(0);
-    load_bias(bias0, bias_next);
+    load_bias(bias0 + ((size_t)kt0 << 11), bias_next);
     __syncthreads();
   }
 
@@ -701,6 +702,22 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       mact[r] = false;
       lsum[r] = 0.f;
       o[r] = zero;
+      if (a.state_in) {
+        // carried state: shift m, sum l (held by the lower half) and unnormalised O
+        const size_t sq = ((size_t)line_of(r) * NH + h) * P + j;
+        const float2 ml = *reinterpret_cast<const float2*>(a.state_ml + 2 * sq);
+        const f32x4* so = reinterpret_cast<const f32x4*>(a.state_o + sq * HD + 16 * hh);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v = so[q4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) o[r][4 * q4 + t] = v[t];
+        }
+        m[r] = ml.x;
+        lsum[r] = hh == 0 ? ml.y : 0.f;
+        qm[r] = unit_frag<T>(hh == 0 ? -ml.x : 0.f);
+        mact[r] = __builtin_amdgcn_ballot_w64(ml.x != 0.f) != 0;
+      }
     }
 
     // One key tile for all rows.  The bias scores (two selector products per
@@ -708,16 +725,16 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
     // K Q^T; -m is a last 16-deep slice.  FIRST: the first tile of the head.
     auto tile = [&](int kt, auto first_tag) {
       constexpr bool FIRST = decltype(first_tag)::value;
-      const int g = h * nkt + kt, buf = g & 1;
+      const int g = h * nbt + kt, buf = g & 1;
       int hn, ktn;
       split(g + 1, hn, ktn);
-      load_tile(hn, ktn);                                   // stage the next tile
+      load_tile(hn, kt0 + ktn);                             // stage the next tile
       f32x16 sbias[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) sbias[st] = mma(esel[0], bias_next[2 * st], zero);
 #pragma unroll
       for (int st = 0; st < 2; ++st) sbias[st] = mma(esel[1], bias_next[2 * st + 1], sbias[st]);
-      load_bias(bias0 + hn * bias_head + ((size_t)ktn << 11), bias_next);
+      load_bias(bias0 + hn * bias_head + ((size_t)(kt0 + ktn) << 11), bias_next);
       // scores of every row first, so that the exponentials of row r run on the
       // VALU while the matrix core still works on row r+1 (and P.V of row r
       // overlaps the exponentials of row r+1)
@@ -739,7 +756,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
           for (int st = 0; st < 2; ++st) sc[r][st] = mma(e0, qm[r], sc[r][st]);
         }
       }
-      if constexpr (FIRST) {
+      if (FIRST && !a.state_in) {                     // (a carried shift stands)
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
           // first tile: shift only if its maximum is far from 0
@@ -780,9 +797,23 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       __syncthreads();
     };
 
-    tile(0, std::true_type{});
-    for (int kt = 1; kt < nkt; ++kt) tile(kt, std::false_type{});
+    if (nbt > 0) tile(0, std::true_type{});
+    for (int kt = 1; kt < nbt; ++kt) tile(kt, std::false_type{});
 
+    if (a.state_out) {
+      // ---- key-block mode: carry (m, l, O) to the next block
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        if (line0 + r >= a.lines) break;
+        const size_t sq = ((size_t)(line0 + r) * NH + h) * P + j;
+        const float lt = xhalf_sum(lsum[r]);
+        f32x4* so = reinterpret_cast<f32x4*>(a.state_o + sq * HD + 16 * hh);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) so[q4] = f32x4{o[r][4 * q4], o[r][4 * q4 + 1], o[r][4 * q4 + 2], o[r][4 * q4 + 3]};
+        if (hh == 0) *reinterpret_cast<float2*>(a.state_ml + 2 * sq) = make_float2(m[r], lt);
+      }
+      continue;
+    }
     // ---- finish head h: 1/l, gate; o^T (e = 16*hh + i) to the workspace
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
@@ -799,7 +830,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
     }
   }
 
-  out_projection<T, ROWS>(a, line0, j, hh, lr);
+  if (!a.state_out) out_projection<T, ROWS>(a, line0, j, hh, lr);
 }
 
 // Bias pack: natural-log fp32 bias [H][I][I] (from K1 or the caller) into the

@@ -78,6 +78,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "triangle_attn_pair_bias": ([P, W, vp, ctypes.c_int32, vp, vp], i32),
         "triangle_attn_project": ([P, i32, W, vp, vp, sz, vp], i32),
         "triangle_attn_attend": ([P, i32, W, vp, vp, vp, sz, vp], i32),
+        "triangle_attn_state_bytes": ([P, i32, ctypes.POINTER(sz)], i32),
+        "triangle_attn_attend_block": ([P, i32, W, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, sz,
+                                        vp], i32),
+        "triangle_attn_attend_finalize": ([P, i32, W, vp, vp, vp, sz, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -220,6 +224,52 @@ def triangle_attn_attend(ws, weights, I, rows, dtype, variant="start", bias=None
         ctypes.byref(problem(I, rows, dtype, eps)), VARIANTS[variant], ctypes.byref(weights_struct(weights, dtype)),
         _ptr(bias), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out
+
+
+def triangle_attn_state_bytes(I: int, rows: int, dtype: torch.dtype, variant: str) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().triangle_attn_state_bytes(ctypes.byref(problem(I, rows, dtype)), VARIANTS[variant],
+                                                    ctypes.byref(n)))
+    return n.value
+
+
+def state(I: int, rows: int, dtype: torch.dtype, variant: str, device=None) -> torch.Tensor:
+    """A carried softmax state buffer for triangle_attn_attend_block (fp32, uninitialised)."""
+    n = triangle_attn_state_bytes(I, rows, dtype, variant)
+    return torch.empty(n // 4, dtype=torch.float32, device=device or "cuda")
+
+
+def triangle_attn_attend_block(ws, weights, I, rows, dtype, key0, nkeys, first, st, variant="start", bias=None,
+                               stream=None, eps=1e-5):
+    """Fold keys [key0, key0 + nkeys) into the carried state `st` (see include/triattn.h)."""
+    _dev(ws, "ws")
+    _dev(st, "state", torch.float32)
+    _check(load_library().triangle_attn_attend_block(
+        ctypes.byref(problem(I, rows, dtype, eps)), VARIANTS[variant], ctypes.byref(weights_struct(weights, dtype)),
+        _ptr(bias), int(key0), int(nkeys), int(bool(first)), _ptr(st), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+    return st
+
+
+def triangle_attn_attend_finalize(ws, weights, I, rows, dtype, st, variant="start", out=None, stream=None,
+                                  eps=1e-5):
+    """o = O / l, gate and output projection of a carried state."""
+    _dev(ws, "ws")
+    _dev(st, "state", torch.float32)
+    out = torch.empty((rows, I, C_Z), dtype=dtype, device=ws.device) if out is None else _dev(out, "out", dtype)
+    _check(load_library().triangle_attn_attend_finalize(
+        ctypes.byref(problem(I, rows, dtype, eps)), VARIANTS[variant], ctypes.byref(weights_struct(weights, dtype)),
+        _ptr(st), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def state_views(st: torch.Tensor, I: int, rows: int, dtype: torch.dtype, variant: str) -> dict:
+    """O [L][H][P][d] and (m, l) [L][H][P][2] views of a state buffer."""
+    lay = triangle_attn_workspace_layout(I, rows, dtype, variant)
+    L, P = lay.lines, lay.positions
+    n_o = L * HEADS * P * HEAD_DIM
+    off_ml = ((n_o * 4 + 255) // 256 * 256) // 4
+    return {"O": st[:n_o].view(L, HEADS, P, HEAD_DIM), "ml": st[off_ml:off_ml + L * HEADS * P * 2].view(L, HEADS, P, 2)}
 
 
 def workspace_views(ws: torch.Tensor, I: int, rows: int, dtype: torch.dtype, variant: str) -> dict:

@@ -40,13 +40,13 @@ def layout(lib, p, variant):
 
 def test_exports_match_header(lib):
     names = ta.header_functions()
-    assert len(names) == 9
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror(lib):
-    assert lib.triangle_attn_abi_version() == 1
+    assert lib.triangle_attn_abi_version() == 2
     for code in range(0, -11, -1):
         msg = lib.triangle_attn_strerror(code).decode()
         assert msg and msg != "unknown error code"
@@ -174,3 +174,42 @@ def test_python_binding_rejects_cpu_tensors():
     z = torch.zeros(4, 4, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ta.triangle_attn_start(z, {})
+
+
+def test_state_bytes(lib):
+    n = ctypes.c_size_t()
+    p = prob(I=1000, dtype=ta.TA_BF16)
+    assert lib.triangle_attn_state_bytes(ctypes.byref(p), ta.TA_START, ctypes.byref(n)) == 0
+    P = 1024
+    o = (1000 * 4 * P * 32 * 4 + 255) // 256 * 256
+    assert n.value == o + (1000 * 4 * P * 2 * 4 + 255) // 256 * 256
+    assert lib.triangle_attn_state_bytes(ctypes.byref(p), ta.TA_START, None) == -1
+    assert lib.triangle_attn_state_bytes(ctypes.byref(prob(I=64, rows=32)), ta.TA_START, ctypes.byref(n)) == -2
+
+
+def test_block_rejects(lib):
+    p = prob(I=200)
+    w = weights()
+    rc, lay = layout(lib, p, ta.TA_START)
+    f = lib.triangle_attn_attend_block
+    call = lambda key0=0, nkeys=64, first=1, st=A + 300 * MB, ws=A + 200 * MB, variant=ta.TA_START, bias=None, \
+        wsb=lay.total: f(ctypes.byref(p), variant, ctypes.byref(w), bias, key0, nkeys, first, st, ws, wsb, None)
+    assert call(key0=32) == -2              # not a multiple of 64
+    assert call(key0=-64) == -2
+    assert call(key0=200) == -2
+    assert call(nkeys=0) == -2
+    assert call(key0=192, nkeys=64) == -2   # past I
+    assert call(key0=64, nkeys=100) == -2   # ragged block that does not end at I
+    assert call(st=None) == -1
+    assert call(st=A + 300 * MB + 4) == -6
+    assert call(st=A + 200 * MB + 4096) == -7   # state inside the workspace
+    assert call(wsb=lay.total - 1) == -5
+    assert call(variant=9) == -9
+    pr = prob(I=200, rows=8)
+    rc, lr = layout(lib, pr, ta.TA_ROWS)
+    assert f(ctypes.byref(pr), ta.TA_ROWS, ctypes.byref(w), None, 0, 64, 1, A + 300 * MB, A + 200 * MB, lr.total,
+             None) == -1                # the first block of a row block needs the bias
+    fin = lib.triangle_attn_attend_finalize
+    assert fin(ctypes.byref(p), ta.TA_START, ctypes.byref(w), None, A + 100 * MB, A + 200 * MB, lay.total, None) == -1
+    assert fin(ctypes.byref(p), ta.TA_START, ctypes.byref(w), A + 300 * MB, A + 200 * MB + 512, A + 200 * MB,
+               lay.total, None) == -7   # out inside the workspace
