@@ -116,6 +116,34 @@ def cpu_baseline(wl, z_host, w_host, target_s=20.0):
                       f"({workers} processes, 1 BLAS thread each), float64 NumPy; {total_t:.1f} s wall"}
 
 
+def key_blocks(ws, wd, I, R, dt, variant, nb, stream, k2_flops, k2_ms, reps=10):
+    """The attention stage as NB key blocks folded into a carried state, then finalize."""
+    import torch
+    from protein_pair_representation_amd import triattn as ta
+    size = ((I + nb - 1) // nb + 63) // 64 * 64     # keys per block: a multiple of 64
+    blocks = [(k0, min(size, I - k0)) for k0 in range(0, I, size)]
+    st = ta.state(I, R, dt, variant)
+    out = torch.empty((R, I, 128), dtype=dt, device="cuda")
+
+    def once():
+        for n, (k0, nk) in enumerate(blocks):
+            ta.triangle_attn_attend_block(ws, wd, I, R, dt, k0, nk, n == 0, st, variant=variant, stream=stream)
+        ta.triangle_attn_attend_finalize(ws, wd, I, R, dt, st, variant=variant, out=out, stream=stream)
+
+    once()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        once()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"variant": variant, "blocks": len(blocks), "block_keys": size, "ms": round(ms, 4),
+            "TFLOP/s": round(k2_flops / (ms * 1e-3) / 1e12, 2), "one_pass_ms": round(k2_ms, 4),
+            "time_vs_one_pass": round(ms / k2_ms, 3)}
+
+
 def _limit_blas():
     from threadpoolctl import threadpool_limits
     threadpool_limits(limits=1)
@@ -242,6 +270,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--key-blocks", type=int, default=4, metavar="NB",
+                    help="also time the key-block stage with NB blocks + finalize (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     ap.add_argument("--summarize-pmc", metavar="DIR",
@@ -365,6 +395,9 @@ def main():
                     "tri_attend": {"avg_launch_ms": round(k2_ms, 4), "TFLOP/s": round(k2_tflops, 2)}},
         "kernel_sha": kernel_sha(),
     }
+    if args.key_blocks > 0 and variants[0] != "rows":
+        res["key_blocks"] = key_blocks(ws[variants[0]], wd, I, R, dt, variants[0], args.key_blocks, stream,
+                                       k2_flops, k2_ms)
     if not args.no_cpu_baseline and z_host is not None:
         res["cpu_baseline"] = cpu_baseline(wl, z_host, w_host)
     print(json.dumps(res), flush=True)
