@@ -218,7 +218,7 @@ def summarize_pmc(run_dir, workload, copy_mib):
                      f"{sum(w) / len(w):12.1f} KiB  -> HBM read {fb / 1e6:9.2f} MB  write {wb / 1e6:9.2f} MB")
     wl_path = os.path.join(PROFILE_DIR, f"tri_attend_{workload}_pmc.txt")
     sha = kernel_sha()
-    cmd_b = f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline"
+    cmd_b = f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline --key-blocks 0"
     cmd_c = f"python3 $R/bench.py --copy-calibration {copy_mib}"
     txt = [f"# HBM traffic per dispatch, workload {workload}, gfx950 (MI355X)",
            "# commands (R = repository root, O = output directory, run from /tmp):",
@@ -248,7 +248,8 @@ def summarize_trace(run_dir, workload, steps, warmup):
     out = [f"# rocprofv3 kernel statistics, workload {workload}, gfx950 (MI355X)",
            "# command (R = repository root, O = output directory, run from /tmp):",
            f"#   timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d $O/kt -o kt -- "
-           f"python3 $R/bench.py --workload {workload} --steps {steps} --warmup {warmup} --no-cpu-baseline",
+           f"python3 $R/bench.py --workload {workload} --steps {steps} --warmup {warmup} --no-cpu-baseline "
+           f"--key-blocks 0",
            f"#   python3 bench.py --summarize-trace $O/kt --workload {workload} --steps {steps} --warmup {warmup}",
            f"# kernel_sha={kernel_sha()}",
            f"{'kernel':16s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
