@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TRIATTN_ABI_VERSION 2
+#define TRIATTN_ABI_VERSION 3
 
 /* Compute dtypes. */
 enum { TA_BF16 = 1, TA_F32 = 2 };
@@ -69,7 +69,8 @@ enum {
   TA_ERR_ALIAS = -7,             /* out overlaps an input or the workspace (out == z is allowed) */
   TA_ERR_HIP = -8,               /* a kernel launch was rejected by the HIP runtime */
   TA_ERR_BAD_VARIANT = -9,
-  TA_ERR_BAD_EPS = -10           /* ln_eps not finite and > 0 */
+  TA_ERR_BAD_EPS = -10,          /* ln_eps not finite and > 0 */
+  TA_ERR_BAD_GROUP = -11         /* AAQ group not A, B or C (include/aaq.h) */
 };
 
 /* Problem description (host memory). */

@@ -1,0 +1,444 @@
+// aaq_kernels.hip -- token-wise adaptive activation quantization (AAQ) of the
+// pair representation on gfx950: encode 128-channel tokens into fixed-size,
+// token-interleaved records, and decode them back.
+//
+// What is computed (LightNobel article, section 2.2; storage, section 2.3.2):
+//  * every token is quantized on its own (2.2.1);
+//  * groups A and B: the 5 channels of largest |x| (equal magnitudes: lower
+//    channel first) are outlier candidates; a candidate is confirmed when
+//    (x - mu)^2 > 9 sigma^2, mu and sigma^2 being the mean and the population
+//    variance of the token's 128 values, in float64 (2.2.2);
+//  * inliers: affine INT8 (group A) or INT4 (groups B, C) over the inlier range
+//    widened to contain 0:  s = (rmax - rmin) / qmax, inv = 1 / s,
+//    z = rint(-rmin * inv), q = clamp(rint(x * inv) + z, 0, qmax), all in
+//    float32, round to nearest even; confirmed outliers: INT16 with their own
+//    scale s_o = max|x_o| / 32767 (2.2.2, 2.2.3);
+//  * decoding: s (q - z), outliers s_o q_o, in float32.
+//
+// Record layout (little endian), tokens back to back:
+//   A 160 B: u8 codes[128] | meta 32 B      B 96 B: u4 codes[128] | meta 32 B
+//   C  80 B: u4 codes[128] | f32 s | u8 z | 11 zero bytes
+//   meta: f32 s | f32 s_o | i16 q_o[5] | u8 channel[5] | u8 z | u8 n | 7 zero bytes
+//   u4 codes: byte j holds channel 2j (low nibble) and 2j+1 (high nibble);
+//   outlier slots in ascending channel order, unused slots zero.
+//
+// Thread mapping: 8 lanes per token, 8 tokens per wave.  With E = 16 / sizeof(T)
+// elements per 16-byte chunk, lane u of a token holds chunks k = 0 .. 16/E - 1,
+// chunk k covering channels 8Ek + Eu .. 8Ek + Eu + E - 1, so one load or store
+// instruction of the wave moves 8 contiguous 128-byte pieces.  Octet reductions
+// use DPP (quad permutes, then the half-row mirror).  The top-5 test runs only
+// for values the 3-sigma test flags: such a value is a candidate exactly when
+// fewer than 5 values of its token rank above it, which a count over the token
+// decides; a token has at most 14 flagged values (at most 1/9 of the values
+// can lie beyond 3 sigma), usually none.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "aaq_kernels.h"
+
+namespace aaq {
+namespace {
+
+constexpr int HZ = 128;
+constexpr int TOPK = 5;
+constexpr int OQMAX = 32767;
+constexpr int LANES = 8;             // lanes per token
+constexpr int VPL = HZ / LANES;      // values per lane
+constexpr int WTOK = 64 / LANES;     // tokens per wave
+constexpr int WAVES = 4;             // waves per workgroup
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Takes the word by value: clang's __builtin_bit_cast applied directly to an
+// element of an ext_vector_type lvalue reads element 0, whatever the index.
+__device__ __forceinline__ float as_float(uint32_t w) { return __builtin_bit_cast(float, w); }
+
+template <int GROUP> struct Fmt;
+template <> struct Fmt<0> { static constexpr int BITS = 8, RB = 160, CB = 128; static constexpr bool OUTL = true; };
+template <> struct Fmt<1> { static constexpr int BITS = 4, RB = 96, CB = 64; static constexpr bool OUTL = true; };
+template <> struct Fmt<2> { static constexpr int BITS = 4, RB = 80, CB = 64; static constexpr bool OUTL = false; };
+
+// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HMIRROR = 0x141;
+
+template <int CTRL> __device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(uint32_t, v)));
+}
+template <int CTRL> __device__ __forceinline__ double dpp(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t r = (uint64_t)dpp<CTRL>((uint32_t)b) | ((uint64_t)dpp<CTRL>((uint32_t)(b >> 32)) << 32);
+  return __builtin_bit_cast(double, r);
+}
+template <int CTRL> __device__ __forceinline__ int dpp(int v) { return (int)dpp<CTRL>((uint32_t)v); }
+
+// Combine the 8 lanes of each token; every lane of the octet ends with the same
+// value (each step combines two equal-sized halves with a commutative op).
+template <typename V, typename Op> __device__ __forceinline__ V octet(V v, Op op) {
+  v = op(v, dpp<DPP_XOR1>(v));
+  v = op(v, dpp<DPP_XOR2>(v));
+  v = op(v, dpp<DPP_HMIRROR>(v));
+  return v;
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<__bf16> { static constexpr int E = 8; };
+template <> struct Elem<float> { static constexpr int E = 4; };
+
+// Channel of value j of lane u.
+template <typename T> __device__ __forceinline__ int chan(int j, int u) {
+  constexpr int E = Elem<T>::E;
+  return (j / E) * (LANES * E) + u * E + (j % E);
+}
+
+template <typename T> __device__ __forceinline__ void unpack(const u32x4& r, float* v);
+template <> __device__ __forceinline__ void unpack<__bf16>(const u32x4& r, float* v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = as_float(r[i] << 16);
+    v[2 * i + 1] = as_float(r[i] & 0xFFFF0000u);
+  }
+}
+template <> __device__ __forceinline__ void unpack<float>(const u32x4& r, float* v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = as_float(r[i]);
+}
+
+template <typename T> __device__ __forceinline__ u32x4 pack(const float* v);
+template <> __device__ __forceinline__ u32x4 pack<__bf16>(const float* v) {
+  __bf16 h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (__bf16)v[i];  // round to nearest even
+  return __builtin_bit_cast(u32x4, h);
+}
+template <> __device__ __forceinline__ u32x4 pack<float>(const float* v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_bit_cast(uint32_t, v[i]);
+  return r;
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Store the E codes of one chunk into the staged record (LDS).
+template <int BITS, int E> __device__ __forceinline__ void put_codes(uint8_t* recp, int c0, const int* q) {
+  if (BITS == 8) {
+    if (E == 8) {
+      uint64_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w |= (uint64_t)q[e] << (8 * e);
+      *reinterpret_cast<uint64_t*>(recp + c0) = w;
+    } else {
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w |= (uint32_t)q[e] << (8 * e);
+      *reinterpret_cast<uint32_t*>(recp + c0) = w;
+    }
+  } else {
+    if (E == 8) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w |= (uint32_t)q[e] << (4 * e);
+      *reinterpret_cast<uint32_t*>(recp + c0 / 2) = w;
+    } else {
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w |= (uint32_t)q[e] << (4 * e);
+      *reinterpret_cast<uint16_t*>(recp + c0 / 2) = (uint16_t)w;
+    }
+  }
+}
+
+template <typename T, int GROUP>
+__global__ void __launch_bounds__(64 * WAVES) aaq_encode(const T* __restrict__ x, int64_t n,
+                                                         uint8_t* __restrict__ rec) {
+#pragma clang fp contract(off)
+  using F = Fmt<GROUP>;
+  constexpr int E = Elem<T>::E, NCH = VPL / E, QMAX = (1 << F::BITS) - 1;
+  constexpr int UNITS = F::RB / 16;  // 16-byte units per record
+  __shared__ __attribute__((aligned(16))) uint8_t stage[WAVES][WTOK * F::RB];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int u = lane & 7, tw = lane >> 3;
+  uint8_t* st = stage[wv];
+  uint8_t* mine = st + tw * F::RB;
+  const int64_t groups = (n + WTOK - 1) / WTOK;
+  for (int64_t g = (int64_t)blockIdx.x * WAVES + wv; g < groups; g += (int64_t)gridDim.x * WAVES) {
+    const int64_t t = g * WTOK + tw;
+    float v[VPL];
+    {
+      const u32x4* src = reinterpret_cast<const u32x4*>(x + t * HZ);
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) {
+        const u32x4 r = t < n ? __builtin_nontemporal_load(src + k * LANES + u) : u32x4{0, 0, 0, 0};
+        unpack<T>(r, v + k * E);
+      }
+    }
+
+    // Section 2.2.2: candidates (top 5 by |x|) confirmed by the 3-sigma rule.
+    uint32_t outm = 0;  // bit j: value j of this lane is a confirmed outlier
+    if (F::OUTL) {
+      double s1 = 0.0;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) s1 += (double)v[j];
+      s1 = octet(s1, [](double a, double b) { return a + b; });
+      const double mu = s1 / 128.0;
+      double s2 = 0.0;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const double d = (double)v[j] - mu;
+        s2 += d * d;
+      }
+      s2 = octet(s2, [](double a, double b) { return a + b; });
+      const double thr = 9.0 * (s2 / 128.0);
+      uint32_t fl = 0;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const double d = (double)v[j] - mu;
+        fl |= (d * d > thr ? 1u : 0u) << j;
+      }
+      // rank test of the flagged values, one per token per round
+      while (__ballot(fl != 0) != 0) {
+        const uint32_t ob = (uint32_t)(__ballot(fl != 0) >> (LANES * tw)) & 0xFFu;
+        const int jj = fl != 0 ? __builtin_ctz(fl) : 0;
+        float a_own = 0.0f;
+        int c_own = 0;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+          if (j == jj) {
+            a_own = fabsf(v[j]);
+            c_own = chan<T>(j, u);
+          }
+        const int src = LANES * tw + (ob != 0 ? __builtin_ctz(ob) : 0);
+        const float a = __shfl(a_own, src);
+        const int c = __shfl(c_own, src);
+        int above = 0;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const float m = fabsf(v[j]);
+          above += (m > a || (m == a && chan<T>(j, u) < c)) ? 1 : 0;
+        }
+        above = octet(above, [](int p, int q) { return p + q; });
+        if (ob != 0 && lane == src) {
+          if (above < TOPK) outm |= 1u << jj;
+          fl &= fl - 1;
+        }
+      }
+    }
+
+    // Inlier range (widened to contain 0), scale, zero point.
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      if (!((outm >> j) & 1u)) {
+        mn = fminf(mn, v[j]);
+        mx = fmaxf(mx, v[j]);
+      }
+    mn = octet(mn, [](float p, float q) { return fminf(p, q); });
+    mx = octet(mx, [](float p, float q) { return fmaxf(p, q); });
+    const float rmin = fminf(mn, 0.0f), rmax = fmaxf(mx, 0.0f);
+    const float s = (rmax - rmin) / (float)QMAX;
+    const float inv = s > 0.0f ? 1.0f / s : 0.0f;
+    const int z = clampi((int)__builtin_rintf(-rmin * inv), 0, QMAX);
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      int q[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int j = k * E + e;
+        q[e] = ((outm >> j) & 1u) ? z : clampi((int)__builtin_rintf(v[j] * inv) + z, 0, QMAX);
+      }
+      put_codes<F::BITS, E>(mine, chan<T>(k * E, u), q);
+    }
+
+    if (F::OUTL) {
+      uint8_t* meta = mine + F::CB;
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j)
+        if ((outm >> j) & 1u) amax = fmaxf(amax, fabsf(v[j]));
+      amax = octet(amax, [](float p, float q) { return fmaxf(p, q); });
+      const float s_o = amax / (float)OQMAX;
+      const float inv_o = s_o > 0.0f ? 1.0f / s_o : 0.0f;
+      int nout = 0;
+      if (__ballot(outm != 0) != 0) {
+        uint32_t w[4] = {0, 0, 0, 0};  // outlier channels of the token, as a 128-bit set
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int c = chan<T>(j, u);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((c >> 5) == i) w[i] |= ((outm >> j) & 1u) << (c & 31);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = octet(w[i], [](uint32_t p, uint32_t q) { return p | q; });
+        nout = __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) +
+               __builtin_popcount(w[3]);
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+          if ((outm >> j) & 1u) {
+            const int c = chan<T>(j, u);
+            int slot = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t below = (c >> 5) > i ? w[i] : ((c >> 5) == i ? (w[i] & ((1u << (c & 31)) - 1u)) : 0u);
+              slot += __builtin_popcount(below);
+            }
+            const int qo = clampi((int)__builtin_rintf(v[j] * inv_o), -OQMAX, OQMAX);
+            if (slot < TOPK) {  // always true: a token has at most TOPK confirmed outliers
+              *reinterpret_cast<int16_t*>(meta + 8 + 2 * slot) = (int16_t)qo;
+              meta[18 + slot] = (uint8_t)c;
+            }
+          }
+      }
+      if (u == 0) {
+        *reinterpret_cast<uint32_t*>(meta) = __builtin_bit_cast(uint32_t, s);
+        *reinterpret_cast<uint32_t*>(meta + 4) = __builtin_bit_cast(uint32_t, s_o);
+        for (int k = nout; k < TOPK; ++k) {
+          *reinterpret_cast<int16_t*>(meta + 8 + 2 * k) = 0;
+          meta[18 + k] = 0;
+        }
+        meta[23] = (uint8_t)z;
+        *reinterpret_cast<uint64_t*>(meta + 24) = (uint64_t)nout;
+      }
+    } else if (u == 0) {
+      uint8_t* meta = mine + F::CB;
+      *reinterpret_cast<uint32_t*>(meta) = __builtin_bit_cast(uint32_t, s);
+      *reinterpret_cast<uint32_t*>(meta + 4) = (uint32_t)z;
+      *reinterpret_cast<uint64_t*>(meta + 8) = 0;
+    }
+
+    // The wave's records leave LDS as contiguous 16-byte units (LDS operations
+    // of one wave complete in program order, so no barrier is needed).
+    const int64_t left = n - g * WTOK;
+    const int nunits = (left < WTOK ? (int)left : WTOK) * UNITS;
+    u32x4* dst = reinterpret_cast<u32x4*>(rec + g * WTOK * F::RB);
+#pragma unroll
+    for (int i = 0; i < (WTOK * UNITS + 63) / 64; ++i) {
+      const int unit = 64 * i + lane;
+      if (unit < nunits) __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(st)[unit], dst + unit);
+    }
+  }
+}
+
+template <typename T, int GROUP>
+__global__ void __launch_bounds__(64 * WAVES) aaq_decode(const uint8_t* __restrict__ rec, int64_t n,
+                                                         T* __restrict__ y) {
+#pragma clang fp contract(off)
+  using F = Fmt<GROUP>;
+  constexpr int E = Elem<T>::E, NCH = VPL / E;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int u = lane & 7, tw = lane >> 3;
+  const int64_t groups = (n + WTOK - 1) / WTOK;
+  for (int64_t g = (int64_t)blockIdx.x * WAVES + wv; g < groups; g += (int64_t)gridDim.x * WAVES) {
+    const int64_t t = g * WTOK + tw;
+    if (t >= n) continue;
+    const uint8_t* r = rec + t * F::RB;
+    const u32x4 m0 = *reinterpret_cast<const u32x4*>(r + F::CB);
+    const float s = as_float(m0[0]);
+    int codes[VPL];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c0 = chan<T>(k * E, u);
+      if (F::BITS == 8) {
+        if (E == 8) {
+          const uint64_t w = *reinterpret_cast<const uint64_t*>(r + c0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) codes[k * E + e] = (int)((w >> (8 * e)) & 0xFF);
+        } else {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(r + c0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) codes[k * E + e] = (int)((w >> (8 * e)) & 0xFF);
+        }
+      } else {
+        const uint32_t w = E == 8 ? *reinterpret_cast<const uint32_t*>(r + c0 / 2)
+                                  : (uint32_t)*reinterpret_cast<const uint16_t*>(r + c0 / 2);
+#pragma unroll
+        for (int e = 0; e < E; ++e) codes[k * E + e] = (int)((w >> (4 * e)) & 0xF);
+      }
+    }
+    u32x4 m1 = {0, 0, 0, 0};
+    if (F::OUTL) m1 = *reinterpret_cast<const u32x4*>(r + F::CB + 16);
+    const int z = F::OUTL ? (int)(m1[1] >> 24) : (int)(m0[1] & 0xFF);  // meta byte 23, or byte 4 (C)
+    float v[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) v[j] = (float)(codes[j] - z) * s;
+    if (F::OUTL) {
+      const int nout = (int)(m1[2] & 0xFF) < TOPK ? (int)(m1[2] & 0xFF) : TOPK;
+      const float s_o = as_float(m0[1]);
+      const uint32_t qw[3] = {m0[2], m0[3], m1[0]};  // i16 q_o[5] at meta bytes 8..17
+      const uint32_t cw[2] = {m1[0] >> 16, m1[1]};      // u8 channel[5] at meta bytes 18..22
+      for (int k = 0; k < nout; ++k) {
+        const int qo = (int)(int16_t)((qw[k >> 1] >> (16 * (k & 1))) & 0xFFFF);
+        const int c = k < 2 ? (int)((cw[0] >> (8 * k)) & 0xFF) : (int)((cw[1] >> (8 * (k - 2))) & 0xFF);
+        const float val = (float)qo * s_o;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+          if (chan<T>(j, u) == c) v[j] = val;
+      }
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(y + t * HZ);
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) __builtin_nontemporal_store(pack<T>(v + k * E), dst + k * LANES + u);
+  }
+}
+
+int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cus[dev] = c;
+  }
+  return cus[dev];
+}
+
+dim3 grid_for(int64_t n) {
+  const int64_t groups = (n + WTOK - 1) / WTOK;
+  const int64_t want = (groups + WAVES - 1) / WAVES;
+  const int64_t cap = (int64_t)cu_count() * 8;
+  return dim3((unsigned)(want < cap ? want : cap));
+}
+
+template <typename T>
+hipError_t encode_t(const void* x, int64_t n, int group, void* rec, hipStream_t s) {
+  const dim3 g = grid_for(n), b(64 * WAVES);
+  const T* xp = static_cast<const T*>(x);
+  uint8_t* rp = static_cast<uint8_t*>(rec);
+  if (group == 0) hipLaunchKernelGGL((aaq_encode<T, 0>), g, b, 0, s, xp, n, rp);
+  else if (group == 1) hipLaunchKernelGGL((aaq_encode<T, 1>), g, b, 0, s, xp, n, rp);
+  else hipLaunchKernelGGL((aaq_encode<T, 2>), g, b, 0, s, xp, n, rp);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t decode_t(const void* rec, int group, int64_t n, void* y, hipStream_t s) {
+  const dim3 g = grid_for(n), b(64 * WAVES);
+  const uint8_t* rp = static_cast<const uint8_t*>(rec);
+  T* yp = static_cast<T*>(y);
+  if (group == 0) hipLaunchKernelGGL((aaq_decode<T, 0>), g, b, 0, s, rp, n, yp);
+  else if (group == 1) hipLaunchKernelGGL((aaq_decode<T, 1>), g, b, 0, s, rp, n, yp);
+  else hipLaunchKernelGGL((aaq_decode<T, 2>), g, b, 0, s, rp, n, yp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int record_bytes(int group) {
+  return group == 0 ? Fmt<0>::RB : group == 1 ? Fmt<1>::RB : group == 2 ? Fmt<2>::RB : -1;
+}
+
+hipError_t launch_encode(const void* x, int dtype, int64_t n, int group, void* rec, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  return dtype == 1 ? encode_t<__bf16>(x, n, group, rec, stream) : encode_t<float>(x, n, group, rec, stream);
+}
+
+hipError_t launch_decode(const void* rec, int group, int64_t n, void* y, int dtype, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  return dtype == 1 ? decode_t<__bf16>(rec, group, n, y, stream) : decode_t<float>(rec, group, n, y, stream);
+}
+
+}  // namespace aaq

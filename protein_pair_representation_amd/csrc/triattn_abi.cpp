@@ -209,6 +209,7 @@ const char* triangle_attn_strerror(int code) {
     case TA_ERR_HIP: return "HIP runtime rejected a kernel launch";
     case TA_ERR_BAD_VARIANT: return "unknown variant";
     case TA_ERR_BAD_EPS: return "ln_eps must be finite and positive";
+    case TA_ERR_BAD_GROUP: return "AAQ group must be AAQ_GROUP_A, _B or _C";
     default: return "unknown error code";
   }
 }

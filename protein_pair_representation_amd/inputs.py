@@ -155,6 +155,42 @@ def random_bias(seed: int, heads: int, I: int, scale: float = 1.0, offset_per_qu
     return torch.from_numpy(b)
 
 
+TOKEN_KINDS = ("gaussian", "offset", "spikes", "tied_spikes", "zeros", "constant", "integers", "tiny")
+
+
+def make_tokens(seed: int, n: int, dtype: str = "bf16", c_z: int = C_Z) -> torch.Tensor:
+    """n synthetic tokens [n][c_z] of mixed shapes, for the quantization codec.
+
+    Token t is of kind TOKEN_KINDS[t % 8]: N(0, 1) scaled by 10^U(-3, 2) per token
+    ("gaussian"); the same plus an offset of 4 sigma, so every value has one sign
+    ("offset"); N(0, 1) with 1 to 8 channels set to +-U(5, 40) ("spikes"); the same
+    with every spike of one magnitude, signs random ("tied_spikes"); all zeros;
+    one value repeated; integers in [-8, 7]; N(0, 1) x 1e-30.  Rounded once
+    (nearest even) to the storage dtype.
+    """
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 11]))
+    x = rng.standard_normal((n, c_z))
+    scale = 10.0 ** rng.uniform(-3, 2, (n, 1))
+    kind = np.arange(n) % len(TOKEN_KINDS)
+    n_sp = rng.integers(1, 9, n)
+    mag = rng.uniform(5, 40, (n, c_z))
+    sign = np.where(rng.random((n, c_z)) < 0.5, -1.0, 1.0)
+    perm = np.argsort(rng.random((n, c_z)), axis=-1)
+    spike = np.zeros((n, c_z), dtype=bool)
+    np.put_along_axis(spike, perm[:, :8], (np.arange(8)[None, :] < n_sp[:, None]), axis=-1)
+    ints = rng.integers(-8, 8, (n, c_z)).astype(np.float64)
+    const = rng.standard_normal((n, 1)) * scale
+    out = x * scale
+    out = np.where((kind == 1)[:, None], (x + 4.0) * scale, out)
+    out = np.where((kind == 2)[:, None], np.where(spike, sign * mag, x), out)
+    out = np.where((kind == 3)[:, None], np.where(spike, sign * mag[:, :1], x), out)
+    out = np.where((kind == 4)[:, None], 0.0, out)
+    out = np.where((kind == 5)[:, None], np.broadcast_to(const, (n, c_z)), out)
+    out = np.where((kind == 6)[:, None], ints, out)
+    out = np.where((kind == 7)[:, None], x * 1e-30, out)
+    return torch.from_numpy(out.astype(np.float32)).to(DTYPES[dtype]).contiguous()
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of stored values (bf16/fp32) to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()

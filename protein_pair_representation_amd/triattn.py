@@ -53,9 +53,12 @@ _lib = None
 
 
 def header_functions() -> list:
-    """Names of the functions include/triattn.h declares."""
-    text = open(os.path.join(ROOT, "include", "triattn.h")).read()
-    return sorted(set(re.findall(r"\b(triangle_attn_\w+)\s*\(", text)))
+    """Names of the functions include/triattn.h and include/aaq.h declare."""
+    names = set()
+    for h in ("triattn.h", "aaq.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        names |= set(re.findall(r"\b((?:triangle_attn|aaq)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
@@ -82,6 +85,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "triangle_attn_attend_block": ([P, i32, W, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, sz,
                                         vp], i32),
         "triangle_attn_attend_finalize": ([P, i32, W, vp, vp, vp, sz, vp], i32),
+        "aaq_record_bytes": ([i32], i32),
+        "aaq_encode": ([vp, i32, ctypes.c_int64, i32, vp, vp], i32),
+        "aaq_decode": ([vp, i32, ctypes.c_int64, vp, i32, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

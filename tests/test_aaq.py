@@ -1,0 +1,132 @@
+"""GPU parity of the AAQ codec (aaq_encode / aaq_decode through the C ABI).
+
+The bar is bit-exactness: both sides take every code-making decision in
+float32 with the same operations, and the 3-sigma test in float64.  The only
+allowed difference is a token whose float64 3-sigma test lies within 1e-9
+(relative) of its threshold, where the two summation orders may decide
+differently; such tokens are counted and left out of the byte comparison, and
+the mixed inputs used here have none.
+Decoding compares the stored outputs (bf16 rounded to nearest even, or fp32)
+bit for bit with the oracle's float32 decode of the same records.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import aaq as oaq
+from protein_pair_representation_amd import aaq, inputs
+
+from test_parity import say
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+NEAR_TIE = 1e-9
+
+
+def tokens_f32(x: torch.Tensor) -> np.ndarray:
+    return x.detach().to("cpu").to(torch.float32).numpy().reshape(-1, 128)
+
+
+def compare_records(got: torch.Tensor, x32: np.ndarray, group: str, what: str):
+    want = oaq.encode(x32, group)
+    got = got.cpu().numpy().reshape(want.shape)
+    ties = oaq.threshold_margin(x32) < NEAR_TIE if group != "C" else np.zeros(len(x32), dtype=bool)
+    assert ties.sum() <= max(1, len(x32) // 10000), f"{what}: {ties.sum()} near-tie tokens"
+    bad = np.flatnonzero(np.any(got != want, axis=1) & ~ties)
+    if len(bad):
+        t = bad[0]
+        diff = np.flatnonzero(got[t] != want[t])
+        raise AssertionError(f"{what}: {len(bad)} records differ; token {t} bytes {diff[:12].tolist()} "
+                             f"got {got[t, diff[:12]].tolist()} want {want[t, diff[:12]].tolist()}")
+    return want
+
+
+def oracle_decoded(rec: np.ndarray, group: str, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(oaq.decode(rec, group)).to(TDT[dtype])
+
+
+def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
+    a, b = a.cpu().contiguous(), b.cpu().contiguous()
+    view = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    return a.shape == b.shape and bool(torch.equal(a.view(view), b.view(view)))
+
+
+@pytest.mark.parametrize("group", ["A", "B", "C"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 64, 1003])
+def test_encode_decode_mixed(group, dtype, n):
+    say(f"[aaq] mixed tokens n={n} {dtype} group {group}")
+    x = inputs.make_tokens(100 + n, n, dtype)
+    x32 = tokens_f32(x)
+    rb = aaq.aaq_record_bytes(group)
+    buf = torch.full((n * rb + 2 * 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    rec = buf[4096:4096 + n * rb].view(n, rb)
+    aaq.aaq_encode(x.cuda(), group, out=rec)
+    for out_dt in ("bf16", "f32"):
+        y = aaq.aaq_decode(rec, group, TDT[out_dt])
+        torch.cuda.synchronize()
+        want_rec = compare_records(rec, x32, group, f"encode {group} {dtype} n={n}")
+        assert same_bits(y, oracle_decoded(want_rec, group, out_dt)), f"decode {group} -> {out_dt}"
+    assert bool(torch.all(buf[:4096] == 0xA5)) and bool(torch.all(buf[-4096:] == 0xA5)), "write outside records"
+
+
+@pytest.mark.parametrize("group", ["A", "B", "C"])
+def test_decode_oracle_records(group):
+    """Records the oracle wrote decode on the GPU exactly as the oracle decodes them."""
+    say(f"[aaq] decode oracle records, group {group}")
+    x32 = tokens_f32(inputs.make_tokens(7, 777, "f32"))
+    rec = oaq.encode(x32, group)
+    for out_dt in ("bf16", "f32"):
+        y = aaq.aaq_decode(torch.from_numpy(rec).cuda(), group, TDT[out_dt])
+        torch.cuda.synchronize()
+        assert same_bits(y, oracle_decoded(rec, group, out_dt)), out_dt
+
+
+def test_hand_record_int8():
+    """The hand-derived INT8 record (scale 1, one INT16 outlier of 4096) on the GPU."""
+    x = np.array([2 * c - 128 for c in range(128)], dtype=np.float32)
+    x[127], x[5] = 127, 4096
+    for dtype in ("bf16", "f32"):
+        xt = torch.from_numpy(x[None]).to(TDT[dtype]).cuda()
+        rec = aaq.aaq_encode(xt, "A")
+        torch.cuda.synchronize()
+        r = rec.cpu().numpy()[0]
+        assert r[5] == 128 and r[127] == 255 and r[0] == 0 and r[64] == 128
+        meta = r[128:]
+        assert meta[:8].tobytes() == bytes.fromhex("0000803f" + "0001003e")
+        assert meta[8:10].tobytes() == bytes.fromhex("ff7f") and meta[18] == 5 and meta[23] == 128 and meta[24] == 1
+        y = aaq.aaq_decode(rec, "A", torch.float32)
+        assert np.array_equal(y.cpu().numpy()[0], x)
+
+
+@pytest.mark.parametrize("wl", ["startend-bf16-I1024-distogram", "start-bf16-I2048-outliers"])
+@pytest.mark.parametrize("group", ["A", "B"])
+def test_workload_tokens(wl, group):
+    """The pair tensor of a workload (its first 512 rows: 0.5M or 1M tokens) in
+    one call; records of sampled rows compared with the oracle byte for byte,
+    and the decode of those rows."""
+    w = inputs.WORKLOADS[wl]
+    nrows = min(w.I, 512)
+    say(f"[aaq] {wl} Z rows 0..{nrows - 1} encoded, group {group}")
+    z = inputs.workload_z(w, 0, nrows)
+    zd = z.cuda()
+    rec = aaq.aaq_encode(zd, group)
+    y = aaq.aaq_decode(rec, group, torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = [0, 1, nrows // 2, nrows - 1]
+    for i in rows:
+        x32 = tokens_f32(z[i])
+        sl = slice(i * w.I, (i + 1) * w.I)
+        want = compare_records(rec[sl], x32, group, f"{wl} row {i}")
+        assert same_bits(y[sl], oracle_decoded(want, group, "bf16")), f"decode row {i}"
+    n_out = oaq.fields(rec[: w.I].cpu().numpy(), group)["n"]
+    say(f"[aaq] row 0: tokens with outliers {np.count_nonzero(n_out)} / {w.I}")
+
+
+def test_zero_tokens_is_a_no_op():
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    rec = aaq.aaq_encode(x, "A")
+    y = aaq.aaq_decode(rec, "A", torch.bfloat16)
+    torch.cuda.synchronize()
+    assert rec.shape == (0, 160) and y.shape == (0, 128)

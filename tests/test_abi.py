@@ -40,14 +40,14 @@ def layout(lib, p, variant):
 
 def test_exports_match_header(lib):
     names = ta.header_functions()
-    assert len(names) == 12
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror(lib):
-    assert lib.triangle_attn_abi_version() == 2
-    for code in range(0, -11, -1):
+    assert lib.triangle_attn_abi_version() == 3
+    for code in range(0, -12, -1):
         msg = lib.triangle_attn_strerror(code).decode()
         assert msg and msg != "unknown error code"
     assert lib.triangle_attn_strerror(-99).decode() == "unknown error code"
@@ -213,3 +213,28 @@ def test_block_rejects(lib):
     assert fin(ctypes.byref(p), ta.TA_START, ctypes.byref(w), None, A + 100 * MB, A + 200 * MB, lay.total, None) == -1
     assert fin(ctypes.byref(p), ta.TA_START, ctypes.byref(w), A + 300 * MB, A + 200 * MB + 512, A + 200 * MB,
                lay.total, None) == -7   # out inside the workspace
+
+
+# ----------------------------------------------------------------------------------------- AAQ codec
+
+def test_aaq_record_bytes(lib):
+    assert [lib.aaq_record_bytes(g) for g in (0, 1, 2)] == [160, 96, 80]
+    assert lib.aaq_record_bytes(3) == -11 and lib.aaq_record_bytes(-1) == -11
+
+
+@pytest.mark.parametrize("x,dtype,n,group,rec,code", [
+    (A, ta.TA_BF16, 8, 3, A + 64 * MB, -11),
+    (A, 3, 8, 0, A + 64 * MB, -4),
+    (A, ta.TA_BF16, -1, 0, A + 64 * MB, -2),
+    (A, ta.TA_BF16, (1 << 40) + 1, 0, A + 64 * MB, -2),
+    (None, ta.TA_BF16, 8, 0, A + 64 * MB, -1),
+    (A, ta.TA_F32, 8, 1, None, -1),
+    (A + 8, ta.TA_BF16, 8, 0, A + 64 * MB, -6),
+    (A, ta.TA_BF16, 8, 2, A + 64 * MB + 4, -6),
+    (A, ta.TA_BF16, 8, 0, A + 1024, -7),       # records start inside x (8 x 256 B)
+    (A + 1024, ta.TA_F32, 8, 0, A, -7),        # x starts inside the records (8 x 160 B)
+    (None, ta.TA_BF16, 0, 0, None, 0),         # n = 0: valid, nothing enqueued
+])
+def test_aaq_rejects(lib, x, dtype, n, group, rec, code):
+    assert lib.aaq_encode(x, dtype, n, group, rec, None) == code
+    assert lib.aaq_decode(rec, group, n, x, dtype, None) == code
