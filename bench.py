@@ -53,8 +53,60 @@ def k2_bytes(I, rows, es):
     return rows * I * 128 * es * 5 + 4 * I * I * es
 
 
-def kernel_sha():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_sha(path=KERNEL_SRC):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+AAQ_SRC = os.path.join(ROOT, "protein_pair_representation_amd", "csrc", "aaq_kernels.hip")
+AAQ_CASES = [("encode", "A"), ("decode", "A"), ("encode", "B"), ("decode", "B")]
+
+
+def aaq_traffic(workload):
+    """{kernel label: HBM bytes per launch} from the committed codec --pmc summary, if current."""
+    path = os.path.join(PROFILE_DIR, f"aaq_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return {}
+    out = {}
+    for m in re.finditer(r"^(aaq_\S+)_traffic_bytes_per_launch=([0-9.eE+]+)\s+kernel_sha=([0-9a-f]+)",
+                         open(path).read(), re.M):
+        if m.group(3) == kernel_sha(AAQ_SRC):
+            out[m.group(1)] = float(m.group(2))
+    return out
+
+
+def aaq_codec(z, workload, stream, reps=20):
+    """The AAQ codec on the workload's pair tensor: encode (bf16 tokens -> records) and
+    decode (records -> bf16 tokens) for groups A and B, each timed over `reps` launches
+    with HIP events on `stream`.  Algorithmic bytes = tokens x (token bytes + record bytes)."""
+    import torch
+    from protein_pair_representation_amd import aaq
+    n = z.numel() // 128
+    tb = 128 * z.element_size()
+    rec = {g: aaq.aaq_encode(z, g, stream=stream) for g in ("A", "B")}
+    y = torch.empty((n, 128), dtype=z.dtype, device=z.device)
+    traffic = aaq_traffic(workload)
+    res = {"tokens": n, "kernel_sha": kernel_sha(AAQ_SRC)}
+    for op, g in AAQ_CASES:
+        def launch():
+            if op == "encode":
+                aaq.aaq_encode(z, g, out=rec[g], stream=stream)
+            else:
+                aaq.aaq_decode(rec[g], g, z.dtype, out=y, stream=stream)
+        launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = n * (tb + aaq.aaq_record_bytes(g))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        label = f"aaq_{op}_{g}_{'bf16' if z.dtype == torch.bfloat16 else 'f32'}"
+        res[label] = {"avg_launch_ms": round(ms, 4), "algorithmic_bytes": nbytes, "GB/s": round(gbs, 1),
+                      "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic.get(label)}
+    return res
 
 
 def read_traffic(workload):
@@ -183,10 +235,13 @@ def _short(name):
     for key in ("tri_attend", "tri_project", "tri_pack_bias", "copyBuffer"):
         if key in name:
             return key
+    m = re.search(r"aaq_(encode|decode)_([ABC])_(bf16|f32)", name)
+    if m:
+        return m.group(0)
     return name[:60]
 
 
-def summarize_pmc(run_dir, workload, copy_mib):
+def summarize_pmc(run_dir, workload, copy_mib, family="tri"):
     """Write the HBM-traffic summary of tri_attend / tri_project from four rocprofv3 --pmc runs.
 
     run_dir holds pmc_fetch/ and pmc_write/ (bench.py under FETCH_SIZE and WRITE_SIZE)
@@ -207,7 +262,7 @@ def summarize_pmc(run_dir, workload, copy_mib):
     per = {}
     for name in sorted(set(kf) | set(kw)):
         sh = _short(name)
-        if not sh.startswith("tri_"):
+        if not sh.startswith(family + "_"):
             continue
         f = kf.get(name, [0.0])
         w = kw.get(name, [0.0])
@@ -216,9 +271,17 @@ def summarize_pmc(run_dir, workload, copy_mib):
         per[sh] = fb + wb
         lines.append(f"{sh:14s} dispatches {len(f):3d}  FETCH_SIZE {sum(f) / len(f):12.1f} KiB  WRITE_SIZE "
                      f"{sum(w) / len(w):12.1f} KiB  -> HBM read {fb / 1e6:9.2f} MB  write {wb / 1e6:9.2f} MB")
-    wl_path = os.path.join(PROFILE_DIR, f"tri_attend_{workload}_pmc.txt")
-    sha = kernel_sha()
-    cmd_b = f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline --key-blocks 0"
+    if family == "aaq":
+        wl_path = os.path.join(PROFILE_DIR, f"aaq_{workload}_pmc.txt")
+        sha = kernel_sha(AAQ_SRC)
+        cmd_b = f"python3 $R/bench.py --workload {workload} --aaq-only --steps 3"
+        tail = [f"{k}_traffic_bytes_per_launch={v:.6e} kernel_sha={sha}" for k, v in sorted(per.items())]
+    else:
+        wl_path = os.path.join(PROFILE_DIR, f"tri_attend_{workload}_pmc.txt")
+        sha = kernel_sha()
+        cmd_b = f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline --key-blocks 0 --aaq 0"
+        tail = [f"traffic_bytes_per_launch={per.get('tri_attend', 0.0):.6e} kernel_sha={sha}",
+                f"tri_project_traffic_bytes_per_launch={per.get('tri_project', 0.0):.6e} kernel_sha={sha}"]
     cmd_c = f"python3 $R/bench.py --copy-calibration {copy_mib}"
     txt = [f"# HBM traffic per dispatch, workload {workload}, gfx950 (MI355X)",
            "# commands (R = repository root, O = output directory, run from /tmp):",
@@ -226,18 +289,17 @@ def summarize_pmc(run_dir, workload, copy_mib):
            f"#   timeout -s KILL 100 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $O/pmc_write -o w -- {cmd_b}",
            f"#   timeout -s KILL 100 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $O/pmc_copy_fetch -o cf -- {cmd_c}",
            f"#   timeout -s KILL 100 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $O/pmc_copy_write -o cw -- {cmd_c}",
-           f"#   python3 bench.py --summarize-pmc $O --workload {workload}",
+           f"#   python3 bench.py --summarize-pmc $O --workload {workload}" + (" --family aaq" if family == "aaq" else ""),
            f"# calibration: a {copy_mib} MiB device copy reads FETCH_SIZE {sum(copy_f) / len(copy_f):.1f} KiB and "
            f"WRITE_SIZE {sum(copy_w) / len(copy_w):.1f} KiB;",
            f"#   scale factors FETCH x{f_scale:.4f}, WRITE x{w_scale:.4f}",
            *lines,
-           f"traffic_bytes_per_launch={per.get('tri_attend', 0.0):.6e} kernel_sha={sha}",
-           f"tri_project_traffic_bytes_per_launch={per.get('tri_project', 0.0):.6e} kernel_sha={sha}"]
+           *tail]
     open(wl_path, "w").write("\n".join(txt) + "\n")
     print("\n".join(txt))
 
 
-def summarize_trace(run_dir, workload, steps, warmup):
+def summarize_trace(run_dir, workload, steps, warmup, family="tri"):
     """Write the per-kernel duration summary from a rocprofv3 --kernel-trace --stats csv run."""
     import csv
     import glob
@@ -245,21 +307,27 @@ def summarize_trace(run_dir, workload, steps, warmup):
     if len(files) != 1:
         raise SystemExit(f"expected one kernel_stats.csv under {run_dir}, found {files}")
     rows = list(csv.DictReader(open(files[0])))
+    if family == "aaq":
+        run = f"python3 $R/bench.py --workload {workload} --aaq-only --steps {steps}"
+        summ = f"python3 bench.py --summarize-trace $O/kt --workload {workload} --steps {steps} --family aaq"
+        sha, path = kernel_sha(AAQ_SRC), os.path.join(PROFILE_DIR, f"aaq_{workload}_trace.txt")
+    else:
+        run = (f"python3 $R/bench.py --workload {workload} --steps {steps} --warmup {warmup} --no-cpu-baseline "
+               f"--key-blocks 0 --aaq 0")
+        summ = f"python3 bench.py --summarize-trace $O/kt --workload {workload} --steps {steps} --warmup {warmup}"
+        sha, path = kernel_sha(), os.path.join(PROFILE_DIR, f"kernels_{workload}_trace.txt")
     out = [f"# rocprofv3 kernel statistics, workload {workload}, gfx950 (MI355X)",
            "# command (R = repository root, O = output directory, run from /tmp):",
-           f"#   timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d $O/kt -o kt -- "
-           f"python3 $R/bench.py --workload {workload} --steps {steps} --warmup {warmup} --no-cpu-baseline "
-           f"--key-blocks 0",
-           f"#   python3 bench.py --summarize-trace $O/kt --workload {workload} --steps {steps} --warmup {warmup}",
-           f"# kernel_sha={kernel_sha()}",
+           f"#   timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d $O/kt -o kt -- {run}",
+           f"#   {summ}",
+           f"# kernel_sha={sha}",
            f"{'kernel':16s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
     for r in rows:
         sh = _short(r["Name"])
-        if not sh.startswith("tri_"):
+        if not sh.startswith(family + "_"):
             continue
         out.append(f"{sh:16s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} {float(r['MinNs']) / 1e3:10.1f} "
                    f"{float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}")
-    path = os.path.join(PROFILE_DIR, f"kernels_{workload}_trace.txt")
     open(path, "w").write("\n".join(out) + "\n")
     print("\n".join(out))
 
@@ -280,12 +348,17 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write the kernel-duration summary under profiles/ from a rocprofv3 --stats run, and exit")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy (--summarize-pmc)")
+    ap.add_argument("--aaq", type=int, default=1, help="also time the AAQ codec on the pair tensor (0: skip)")
+    ap.add_argument("--aaq-only", action="store_true",
+                    help="time only the AAQ codec (encode/decode, groups A and B) over --steps launches each")
+    ap.add_argument("--family", default="tri", choices=["tri", "aaq"],
+                    help="kernel family of --summarize-pmc / --summarize-trace")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc, args.workload, args.copy_mib)
+        summarize_pmc(args.summarize_pmc, args.workload, args.copy_mib, args.family)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.workload, args.steps, args.warmup)
+        summarize_trace(args.summarize_trace, args.workload, args.steps, args.warmup, args.family)
         return
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -332,6 +405,9 @@ def main():
         z = z_host.to(dev)
         bias = None
     torch.cuda.synchronize()
+    if args.aaq_only:
+        print(json.dumps({"workload": wl.name, "aaq": aaq_codec(z, wl.name, stream, reps=args.steps)}), flush=True)
+        return
 
     ws = {v: ta.workspace(I, R, dt, v, dev) for v in variants}
     out = {v: torch.empty((R, I, 128), dtype=dt, device=dev) for v in variants}
@@ -399,6 +475,8 @@ def main():
     if args.key_blocks > 0 and variants[0] != "rows":
         res["key_blocks"] = key_blocks(ws[variants[0]], wd, I, R, dt, variants[0], args.key_blocks, stream,
                                        k2_flops, k2_ms)
+    if args.aaq > 0:
+        res["aaq"] = aaq_codec(z, wl.name, stream)
     if not args.no_cpu_baseline and z_host is not None:
         res["cpu_baseline"] = cpu_baseline(wl, z_host, w_host)
     print(json.dumps(res), flush=True)

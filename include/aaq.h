@@ -10,7 +10,7 @@
  *    |x| (equal magnitudes: the lower channel first) are candidates; a
  *    candidate is confirmed when |x - mu| > 3 sigma, mu and sigma being the
  *    mean and the population standard deviation of the token's 128 values,
- *    evaluated in float64 as (x - mu)^2 > 9 sigma^2.  Confirmed outliers are
+ *    all in float64 (sigma = sqrt of the two-pass variance).  Confirmed outliers are
  *    stored as INT16 with a scale of their own: s_o = max|x_o| / 32767,
  *    q_o = clamp(rint(x / s_o), -32767, 32767).
  *  - The other values (inliers) are quantized affinely (section 2.2.3: group A

@@ -23,8 +23,7 @@ Readings where the article is silent (each one a line of the design notes):
 * candidates are ranked by |x|; equal magnitudes go to the lower channel;
 * the 3-sigma rule uses the mean mu and the population standard deviation
   sigma of all Hz values of the token (float64, two passes); a candidate is
-  confirmed when |x - mu| > 3 sigma, evaluated as (x - mu)^2 > 9 sigma^2 so
-  that no square root enters the decision;
+  confirmed when |x - mu| > 3 sigma, sigma = sqrt(variance), in float64;
 * inliers: affine (asymmetric) uniform quantization with an integer zero point
   over the inlier range widened to contain 0, so that 0 is exact and the zero
   point fits the code range -- the scheme of Jacob et al., "Quantization and
@@ -103,7 +102,7 @@ def confirm_outliers(x: np.ndarray, cand: np.ndarray) -> np.ndarray:
     mu, var = token_stats(x)
     xc = np.take_along_axis(x, cand, axis=-1).astype(np.float64)
     d = xc - mu[:, None]
-    ok = d * d > (SIGMA_RULE * SIGMA_RULE) * var[:, None]
+    ok = np.abs(d) > SIGMA_RULE * np.sqrt(var)[:, None]
     mask = np.zeros(x.shape, dtype=bool)
     np.put_along_axis(mask, cand, ok, axis=-1)
     return mask
@@ -228,13 +227,13 @@ def fields(rec: np.ndarray, group: str) -> dict:
 
 
 def threshold_margin(x: np.ndarray) -> np.ndarray:
-    """Per token, the smallest relative distance |d^2 - 9 var| / (9 var) over its top-k
-    candidates: how close the float64 3-sigma decisions came to their threshold."""
+    """Per token, the smallest relative distance ||x - mu| - 3 sigma| / (3 sigma) over its
+    top-k candidates: how close the float64 3-sigma decisions came to their threshold."""
     x = np.asarray(x, dtype=f32).reshape(-1, HZ)
     cand = topk_candidates(x)
     mu, var = token_stats(x)
     d = np.take_along_axis(x, cand, axis=-1).astype(np.float64) - mu[:, None]
-    thr = (SIGMA_RULE * SIGMA_RULE) * var[:, None]
+    thr = SIGMA_RULE * np.sqrt(var)[:, None]
     with np.errstate(divide="ignore", invalid="ignore"):
-        m = np.abs(d * d - thr) / thr
+        m = np.abs(np.abs(d) - thr) / thr
     return np.where(thr > 0, m, np.inf).min(axis=-1)

@@ -6,8 +6,8 @@
 //  * every token is quantized on its own (2.2.1);
 //  * groups A and B: the 5 channels of largest |x| (equal magnitudes: lower
 //    channel first) are outlier candidates; a candidate is confirmed when
-//    (x - mu)^2 > 9 sigma^2, mu and sigma^2 being the mean and the population
-//    variance of the token's 128 values, in float64 (2.2.2);
+//    |x - mu| > 3 sigma, mu and sigma being the mean and the population
+//    standard deviation of the token's 128 values, in float64 (2.2.2);
 //  * inliers: affine INT8 (group A) or INT4 (groups B, C) over the inlier range
 //    widened to contain 0:  s = (rmax - rmin) / qmax, inv = 1 / s,
 //    z = rint(-rmin * inv), q = clamp(rint(x * inv) + z, 0, qmax), all in
@@ -26,11 +26,14 @@
 // elements per 16-byte chunk, lane u of a token holds chunks k = 0 .. 16/E - 1,
 // chunk k covering channels 8Ek + Eu .. 8Ek + Eu + E - 1, so one load or store
 // instruction of the wave moves 8 contiguous 128-byte pieces.  Octet reductions
-// use DPP (quad permutes, then the half-row mirror).  The top-5 test runs only
-// for values the 3-sigma test flags: such a value is a candidate exactly when
-// fewer than 5 values of its token rank above it, which a count over the token
-// decides; a token has at most 14 flagged values (at most 1/9 of the values
-// can lie beyond 3 sigma), usually none.
+// use DPP (quad permutes, then the half-row mirror).  Outliers are confirmed
+// candidates, i.e. values flagged by the 3-sigma test that rank among the top 5
+// by |x|; so only flagged values are ranked (a token has at most 14 of them --
+// at most 1/9 of the values can lie beyond 3 sigma -- usually none or one).  A
+// single count settles a whole token when at most 5 of its values reach the
+// smallest flagged |x|; other tokens rank their flagged values one at a time.
+// Outlier values are then set to 0, which codes as the zero point z and keeps
+// the inlier range (widened to contain 0) unchanged.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -151,18 +154,28 @@ template <int BITS, int E> __device__ __forceinline__ void put_codes(uint8_t* re
   }
 }
 
+// Channels of lane u's chunk k occupy E consecutive bits of the token's 128-bit
+// channel set, inside 64-bit word (k * 8E) / 64 at bit (k * 8E + u E) % 64.
+template <typename T> __device__ __forceinline__ void chunk_bits(uint64_t* w, int k, int u, uint32_t bits) {
+  constexpr int E = Elem<T>::E;
+  const int c0 = k * LANES * E + u * E;
+  w[c0 >> 6] |= (uint64_t)bits << (c0 & 63);
+}
+
 template <typename T, int GROUP>
-__global__ void __launch_bounds__(64 * WAVES) aaq_encode(const T* __restrict__ x, int64_t n,
-                                                         uint8_t* __restrict__ rec) {
+__device__ __forceinline__ void encode_body(const T* __restrict__ x, int64_t n, uint8_t* __restrict__ rec) {
 #pragma clang fp contract(off)
   using F = Fmt<GROUP>;
   constexpr int E = Elem<T>::E, NCH = VPL / E, QMAX = (1 << F::BITS) - 1;
   constexpr int UNITS = F::RB / 16;  // 16-byte units per record
   __shared__ __attribute__((aligned(16))) uint8_t stage[WAVES][WTOK * F::RB];
+  // each lane's values, for the few steps that index them by a per-lane position
+  __shared__ __attribute__((aligned(16))) float spill[F::OUTL ? WAVES : 1][F::OUTL ? 64 * VPL : 4];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int u = lane & 7, tw = lane >> 3;
   uint8_t* st = stage[wv];
   uint8_t* mine = st + tw * F::RB;
+  float* myv = &spill[F::OUTL ? wv : 0][F::OUTL ? lane * VPL : 0];
   const int64_t groups = (n + WTOK - 1) / WTOK;
   for (int64_t g = (int64_t)blockIdx.x * WAVES + wv; g < groups; g += (int64_t)gridDim.x * WAVES) {
     const int64_t t = g * WTOK + tw;
@@ -176,123 +189,142 @@ __global__ void __launch_bounds__(64 * WAVES) aaq_encode(const T* __restrict__ x
       }
     }
 
-    // Section 2.2.2: candidates (top 5 by |x|) confirmed by the 3-sigma rule.
-    uint32_t outm = 0;  // bit j: value j of this lane is a confirmed outlier
+    float s_o = 0.0f;
+    int nout = 0;
     if (F::OUTL) {
+      // Section 2.2.2.  Mean and population deviation of the token (float64, two passes);
+      // flagged: |x - mu| > 3 sigma.
+      double d[VPL];
       double s1 = 0.0;
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) s1 += (double)v[j];
+      for (int j = 0; j < VPL; ++j) {
+        d[j] = (double)v[j];
+        s1 += d[j];
+      }
       s1 = octet(s1, [](double a, double b) { return a + b; });
       const double mu = s1 / 128.0;
       double s2 = 0.0;
 #pragma unroll
       for (int j = 0; j < VPL; ++j) {
-        const double d = (double)v[j] - mu;
-        s2 += d * d;
+        d[j] = d[j] - mu;
+        s2 = __builtin_fma(d[j], d[j], s2);
       }
       s2 = octet(s2, [](double a, double b) { return a + b; });
-      const double thr = 9.0 * (s2 / 128.0);
+      const double lim = 3.0 * __builtin_sqrt(s2 / 128.0);
       uint32_t fl = 0;
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        const double d = (double)v[j] - mu;
-        fl |= (d * d > thr ? 1u : 0u) << j;
-      }
-      // rank test of the flagged values, one per token per round
-      while (__ballot(fl != 0) != 0) {
-        const uint32_t ob = (uint32_t)(__ballot(fl != 0) >> (LANES * tw)) & 0xFFu;
-        const int jj = fl != 0 ? __builtin_ctz(fl) : 0;
-        float a_own = 0.0f;
-        int c_own = 0;
+      for (int j = 0; j < VPL; ++j) fl |= (__builtin_fabs(d[j]) > lim ? 1u : 0u) << j;
+
+      uint32_t outm = 0;  // bit j: value j of this lane is a confirmed outlier
+      if (__ballot(fl != 0) != 0) {
 #pragma unroll
-        for (int j = 0; j < VPL; ++j)
-          if (j == jj) {
-            a_own = fabsf(v[j]);
-            c_own = chan<T>(j, u);
-          }
-        const int src = LANES * tw + (ob != 0 ? __builtin_ctz(ob) : 0);
-        const float a = __shfl(a_own, src);
-        const int c = __shfl(c_own, src);
-        int above = 0;
+        for (int q = 0; q < VPL / 4; ++q)
+          *reinterpret_cast<float4*>(myv + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        // A flagged value is a candidate when fewer than 5 values of its token rank
+        // above it.  Fast test for the whole token: if at most 5 values have |x| at
+        // least the smallest flagged |x|, every flagged value is a candidate.
+        float amin = __builtin_inff();
+        for (uint32_t b = fl; b != 0; b &= b - 1) amin = fminf(amin, fabsf(myv[__builtin_ctz(b)]));
+        amin = octet(amin, [](float p, float q) { return fminf(p, q); });
+        int cnt = 0;
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-          const float m = fabsf(v[j]);
-          above += (m > a || (m == a && chan<T>(j, u) < c)) ? 1 : 0;
+        for (int j = 0; j < VPL; ++j) cnt += fabsf(v[j]) >= amin ? 1 : 0;
+        cnt = octet(cnt, [](int p, int q) { return p + q; });
+        if (cnt <= TOPK) {
+          outm = fl;
+          fl = 0;
         }
-        above = octet(above, [](int p, int q) { return p + q; });
-        if (ob != 0 && lane == src) {
-          if (above < TOPK) outm |= 1u << jj;
-          fl &= fl - 1;
+        // Otherwise rank each flagged value: one per token per round.
+        while (__ballot(fl != 0) != 0) {
+          const uint32_t ob = (uint32_t)(__ballot(fl != 0) >> (LANES * tw)) & 0xFFu;
+          const int jj = fl != 0 ? __builtin_ctz(fl) : 0;
+          const float a_own = fabsf(myv[jj]);
+          const int c_own = (jj / E) * (LANES * E) + u * E + (jj % E);
+          const int src = LANES * tw + (ob != 0 ? __builtin_ctz(ob) : 0);
+          const float a = __shfl(a_own, src);
+          const int c = __shfl(c_own, src);
+          int above = 0;
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            const float m = fabsf(v[j]);
+            above += (m > a || (m == a && chan<T>(j, u) < c)) ? 1 : 0;
+          }
+          above = octet(above, [](int p, int q) { return p + q; });
+          if (ob != 0 && lane == src) {
+            if (above < TOPK) outm |= 1u << jj;
+            fl &= fl - 1;
+          }
+        }
+      }
+
+      if (__ballot(outm != 0) != 0) {
+        // INT16 outliers with their own scale; slots in ascending channel order.
+        float am = 0.0f;
+        for (uint32_t b = outm; b != 0; b &= b - 1) am = fmaxf(am, fabsf(myv[__builtin_ctz(b)]));
+        am = octet(am, [](float p, float q) { return fmaxf(p, q); });
+        s_o = am / (float)OQMAX;
+        const float inv_o = s_o > 0.0f ? 1.0f / s_o : 0.0f;
+        uint64_t w[2] = {0, 0};
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) chunk_bits<T>(w, k, u, (outm >> (k * E)) & ((1u << E) - 1u));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          uint32_t lo = (uint32_t)w[i], hi = (uint32_t)(w[i] >> 32);
+          lo = octet(lo, [](uint32_t p, uint32_t q) { return p | q; });
+          hi = octet(hi, [](uint32_t p, uint32_t q) { return p | q; });
+          w[i] = (uint64_t)lo | ((uint64_t)hi << 32);
+        }
+        nout = __builtin_popcountll(w[0]) + __builtin_popcountll(w[1]);
+        uint8_t* meta = mine + F::CB;
+        for (uint32_t b = outm; b != 0; b &= b - 1) {
+          const int j = __builtin_ctz(b);
+          const int c = (j / E) * (LANES * E) + u * E + (j % E);
+          const int slot = c < 64 ? __builtin_popcountll(w[0] & ((1ull << c) - 1ull))
+                                  : __builtin_popcountll(w[0]) +
+                                        __builtin_popcountll(w[1] & ((1ull << (c - 64)) - 1ull));
+          const int qo = clampi((int)__builtin_rintf(myv[j] * inv_o), -OQMAX, OQMAX);
+          if (slot < TOPK) {  // always true: a token has at most TOPK confirmed outliers
+            *reinterpret_cast<int16_t*>(meta + 8 + 2 * slot) = (int16_t)qo;
+            meta[18 + slot] = (uint8_t)c;
+          }
+          myv[j] = 0.0f;  // an outlier's channel codes as z, the code of 0
+        }
+#pragma unroll
+        for (int q = 0; q < VPL / 4; ++q) {
+          const float4 f4 = *reinterpret_cast<const float4*>(myv + 4 * q);
+          v[4 * q] = f4.x;
+          v[4 * q + 1] = f4.y;
+          v[4 * q + 2] = f4.z;
+          v[4 * q + 3] = f4.w;
         }
       }
     }
 
-    // Inlier range (widened to contain 0), scale, zero point.
-    float mn = __builtin_inff(), mx = -__builtin_inff();
+    // Inlier range widened to contain 0 (outliers are 0 now), scale, zero point.
+    float mn = 0.0f, mx = 0.0f;
 #pragma unroll
-    for (int j = 0; j < VPL; ++j)
-      if (!((outm >> j) & 1u)) {
-        mn = fminf(mn, v[j]);
-        mx = fmaxf(mx, v[j]);
-      }
-    mn = octet(mn, [](float p, float q) { return fminf(p, q); });
-    mx = octet(mx, [](float p, float q) { return fmaxf(p, q); });
-    const float rmin = fminf(mn, 0.0f), rmax = fmaxf(mx, 0.0f);
+    for (int j = 0; j < VPL; ++j) {
+      mn = fminf(mn, v[j]);
+      mx = fmaxf(mx, v[j]);
+    }
+    const float rmin = octet(mn, [](float p, float q) { return fminf(p, q); });
+    const float rmax = octet(mx, [](float p, float q) { return fmaxf(p, q); });
     const float s = (rmax - rmin) / (float)QMAX;
     const float inv = s > 0.0f ? 1.0f / s : 0.0f;
-    const int z = clampi((int)__builtin_rintf(-rmin * inv), 0, QMAX);
+    const float zf = __builtin_rintf(-rmin * inv);  // in [0, QMAX]: rmin <= 0 <= rmax
+    const int z = (int)zf;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       int q[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int j = k * E + e;
-        q[e] = ((outm >> j) & 1u) ? z : clampi((int)__builtin_rintf(v[j] * inv) + z, 0, QMAX);
-      }
+      for (int e = 0; e < E; ++e)
+        q[e] = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(v[k * E + e] * inv) + zf, 0.0f, (float)QMAX);
       put_codes<F::BITS, E>(mine, chan<T>(k * E, u), q);
     }
 
     if (F::OUTL) {
-      uint8_t* meta = mine + F::CB;
-      float amax = 0.0f;
-#pragma unroll
-      for (int j = 0; j < VPL; ++j)
-        if ((outm >> j) & 1u) amax = fmaxf(amax, fabsf(v[j]));
-      amax = octet(amax, [](float p, float q) { return fmaxf(p, q); });
-      const float s_o = amax / (float)OQMAX;
-      const float inv_o = s_o > 0.0f ? 1.0f / s_o : 0.0f;
-      int nout = 0;
-      if (__ballot(outm != 0) != 0) {
-        uint32_t w[4] = {0, 0, 0, 0};  // outlier channels of the token, as a 128-bit set
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-          const int c = chan<T>(j, u);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if ((c >> 5) == i) w[i] |= ((outm >> j) & 1u) << (c & 31);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = octet(w[i], [](uint32_t p, uint32_t q) { return p | q; });
-        nout = __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) +
-               __builtin_popcount(w[3]);
-#pragma unroll
-        for (int j = 0; j < VPL; ++j)
-          if ((outm >> j) & 1u) {
-            const int c = chan<T>(j, u);
-            int slot = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t below = (c >> 5) > i ? w[i] : ((c >> 5) == i ? (w[i] & ((1u << (c & 31)) - 1u)) : 0u);
-              slot += __builtin_popcount(below);
-            }
-            const int qo = clampi((int)__builtin_rintf(v[j] * inv_o), -OQMAX, OQMAX);
-            if (slot < TOPK) {  // always true: a token has at most TOPK confirmed outliers
-              *reinterpret_cast<int16_t*>(meta + 8 + 2 * slot) = (int16_t)qo;
-              meta[18 + slot] = (uint8_t)c;
-            }
-          }
-      }
       if (u == 0) {
+        uint8_t* meta = mine + F::CB;
         *reinterpret_cast<uint32_t*>(meta) = __builtin_bit_cast(uint32_t, s);
         *reinterpret_cast<uint32_t*>(meta + 4) = __builtin_bit_cast(uint32_t, s_o);
         for (int k = nout; k < TOPK; ++k) {
@@ -323,8 +355,7 @@ __global__ void __launch_bounds__(64 * WAVES) aaq_encode(const T* __restrict__ x
 }
 
 template <typename T, int GROUP>
-__global__ void __launch_bounds__(64 * WAVES) aaq_decode(const uint8_t* __restrict__ rec, int64_t n,
-                                                         T* __restrict__ y) {
+__device__ __forceinline__ void decode_body(const uint8_t* __restrict__ rec, int64_t n, T* __restrict__ y) {
 #pragma clang fp contract(off)
   using F = Fmt<GROUP>;
   constexpr int E = Elem<T>::E, NCH = VPL / E;
@@ -384,6 +415,23 @@ __global__ void __launch_bounds__(64 * WAVES) aaq_decode(const uint8_t* __restri
   }
 }
 
+#define AAQ_KERNELS(GN, G, TN, T)                                                                    \
+  __global__ void __launch_bounds__(64 * WAVES)                                                      \
+      aaq_encode_##GN##_##TN(const T* __restrict__ x, int64_t n, uint8_t* __restrict__ rec) {        \
+    encode_body<T, G>(x, n, rec);                                                                    \
+  }                                                                                                  \
+  __global__ void __launch_bounds__(64 * WAVES)                                                      \
+      aaq_decode_##GN##_##TN(const uint8_t* __restrict__ rec, int64_t n, T* __restrict__ y) {        \
+    decode_body<T, G>(rec, n, y);                                                                    \
+  }
+AAQ_KERNELS(A, 0, bf16, __bf16)
+AAQ_KERNELS(B, 1, bf16, __bf16)
+AAQ_KERNELS(C, 2, bf16, __bf16)
+AAQ_KERNELS(A, 0, f32, float)
+AAQ_KERNELS(B, 1, f32, float)
+AAQ_KERNELS(C, 2, f32, float)
+#undef AAQ_KERNELS
+
 int cu_count() {
   static int cus[64] = {0};
   int dev = 0;
@@ -403,25 +451,37 @@ dim3 grid_for(int64_t n) {
   return dim3((unsigned)(want < cap ? want : cap));
 }
 
-template <typename T>
-hipError_t encode_t(const void* x, int64_t n, int group, void* rec, hipStream_t s) {
+hipError_t launch_enc(int dtype, int group, const void* x, int64_t n, void* rec, hipStream_t s) {
   const dim3 g = grid_for(n), b(64 * WAVES);
-  const T* xp = static_cast<const T*>(x);
   uint8_t* rp = static_cast<uint8_t*>(rec);
-  if (group == 0) hipLaunchKernelGGL((aaq_encode<T, 0>), g, b, 0, s, xp, n, rp);
-  else if (group == 1) hipLaunchKernelGGL((aaq_encode<T, 1>), g, b, 0, s, xp, n, rp);
-  else hipLaunchKernelGGL((aaq_encode<T, 2>), g, b, 0, s, xp, n, rp);
+  if (dtype == 1) {
+    const __bf16* xp = static_cast<const __bf16*>(x);
+    if (group == 0) hipLaunchKernelGGL(aaq_encode_A_bf16, g, b, 0, s, xp, n, rp);
+    else if (group == 1) hipLaunchKernelGGL(aaq_encode_B_bf16, g, b, 0, s, xp, n, rp);
+    else hipLaunchKernelGGL(aaq_encode_C_bf16, g, b, 0, s, xp, n, rp);
+  } else {
+    const float* xp = static_cast<const float*>(x);
+    if (group == 0) hipLaunchKernelGGL(aaq_encode_A_f32, g, b, 0, s, xp, n, rp);
+    else if (group == 1) hipLaunchKernelGGL(aaq_encode_B_f32, g, b, 0, s, xp, n, rp);
+    else hipLaunchKernelGGL(aaq_encode_C_f32, g, b, 0, s, xp, n, rp);
+  }
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t decode_t(const void* rec, int group, int64_t n, void* y, hipStream_t s) {
+hipError_t launch_dec(int dtype, int group, const void* rec, int64_t n, void* y, hipStream_t s) {
   const dim3 g = grid_for(n), b(64 * WAVES);
   const uint8_t* rp = static_cast<const uint8_t*>(rec);
-  T* yp = static_cast<T*>(y);
-  if (group == 0) hipLaunchKernelGGL((aaq_decode<T, 0>), g, b, 0, s, rp, n, yp);
-  else if (group == 1) hipLaunchKernelGGL((aaq_decode<T, 1>), g, b, 0, s, rp, n, yp);
-  else hipLaunchKernelGGL((aaq_decode<T, 2>), g, b, 0, s, rp, n, yp);
+  if (dtype == 1) {
+    __bf16* yp = static_cast<__bf16*>(y);
+    if (group == 0) hipLaunchKernelGGL(aaq_decode_A_bf16, g, b, 0, s, rp, n, yp);
+    else if (group == 1) hipLaunchKernelGGL(aaq_decode_B_bf16, g, b, 0, s, rp, n, yp);
+    else hipLaunchKernelGGL(aaq_decode_C_bf16, g, b, 0, s, rp, n, yp);
+  } else {
+    float* yp = static_cast<float*>(y);
+    if (group == 0) hipLaunchKernelGGL(aaq_decode_A_f32, g, b, 0, s, rp, n, yp);
+    else if (group == 1) hipLaunchKernelGGL(aaq_decode_B_f32, g, b, 0, s, rp, n, yp);
+    else hipLaunchKernelGGL(aaq_decode_C_f32, g, b, 0, s, rp, n, yp);
+  }
   return hipGetLastError();
 }
 
@@ -433,12 +493,12 @@ int record_bytes(int group) {
 
 hipError_t launch_encode(const void* x, int dtype, int64_t n, int group, void* rec, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  return dtype == 1 ? encode_t<__bf16>(x, n, group, rec, stream) : encode_t<float>(x, n, group, rec, stream);
+  return launch_enc(dtype, group, x, n, rec, stream);
 }
 
 hipError_t launch_decode(const void* rec, int group, int64_t n, void* y, int dtype, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  return dtype == 1 ? decode_t<__bf16>(rec, group, n, y, stream) : decode_t<float>(rec, group, n, y, stream);
+  return launch_dec(dtype, group, rec, n, y, stream);
 }
 
 }  // namespace aaq

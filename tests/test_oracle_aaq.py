@@ -265,7 +265,7 @@ def _mut_two_sigma(_orig):
     def f(x, cand):
         mu, var = aaq.token_stats(x)
         xc = np.take_along_axis(x, cand, axis=-1).astype(np.float64)
-        ok = (xc - mu[:, None]) ** 2 > 4.0 * var[:, None]
+        ok = np.abs(xc - mu[:, None]) > 2.0 * np.sqrt(var)[:, None]
         mask = np.zeros(x.shape, dtype=bool)
         np.put_along_axis(mask, cand, ok, axis=-1)
         return mask
