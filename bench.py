@@ -109,6 +109,32 @@ def aaq_codec(z, workload, stream, reps=20):
     return res
 
 
+def aaq_project(z, wd, variant, stream, reps=20):
+    """The projection stage (K1 + bias pack) fed by the pair tensor as bf16 tokens and
+    as group-A records, each timed over `reps` calls with HIP events on `stream`."""
+    import torch
+    from protein_pair_representation_amd import aaq
+    from protein_pair_representation_amd import triattn as ta
+    R, I = z.shape[0], z.shape[1]
+    rec = aaq.aaq_encode(z, "A", stream=stream)
+    ws = ta.workspace(I, R, z.dtype, variant, z.device)
+    runs = {"from_bf16_tokens": lambda: ta.triangle_attn_project(z, wd, variant=variant, ws=ws, stream=stream),
+            "from_group_a_records": lambda: ta.triangle_attn_project_aaq(rec, wd, I, R, "A", variant=variant, ws=ws,
+                                                                         stream=stream)}
+    out = {"variant": variant}
+    for name, fn in runs.items():
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name + "_ms"] = round(e0.elapsed_time(e1) / reps, 4)
+    return out
+
+
 def read_traffic(workload):
     """HBM bytes per tri_attend launch from the committed rocprofv3 --pmc summary, if current."""
     path = os.path.join(PROFILE_DIR, f"tri_attend_{workload}_pmc.txt")
@@ -477,6 +503,8 @@ def main():
                                        k2_flops, k2_ms)
     if args.aaq > 0:
         res["aaq"] = aaq_codec(z, wl.name, stream)
+        if wl.dtype == "bf16":
+            res["aaq"]["project_stage"] = aaq_project(z, wd, variants[0], stream)
     if not args.no_cpu_baseline and z_host is not None:
         res["cpu_baseline"] = cpu_baseline(wl, z_host, w_host)
     print(json.dumps(res), flush=True)

@@ -78,6 +78,25 @@ int aaq_encode(const void* x, int dtype, int64_t n, int group, void* records, vo
  * Errors as for aaq_encode (TA_ERR_ALIAS: y overlaps records). */
 int aaq_decode(const void* records, int group, int64_t n, void* y, int dtype, void* stream);
 
+/* Stage 1 of triangle attention (as triangle_attn_project, include/triattn.h)
+ * reading the pair tensor as token-wise quantized records instead of bf16
+ * tokens: the pair tensor is on the residual path, the activations the
+ * LightNobel article (section 2.2.3) keeps in group A.  Each token is decoded
+ * in registers -- s (q - z), outliers s_o q_o, in fp32 exactly as aaq_decode
+ * computes them -- and LayerNorm and the projections run on those fp32 values.
+ *   prob     as for triangle_attn_project; dtype must be TA_BF16 (bf16 weights
+ *            and workspace)
+ *   records  [rows][I] records of `group` (A, B or C), token (i, j) at
+ *            records + (i * I + j) * aaq_record_bytes(group); for TA_END the
+ *            ending-node lines are the columns of this array, as for z
+ *   ws       the workspace of triangle_attn_project; triangle_attn_attend then
+ *            runs on it unchanged
+ * Errors as for triangle_attn_project, plus TA_ERR_BAD_DTYPE (not bf16) and
+ * TA_ERR_BAD_GROUP. */
+int triangle_attn_project_aaq(const ta_problem* prob, int variant, const ta_weights* w,
+                              const void* records, int group, void* ws, size_t ws_bytes,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

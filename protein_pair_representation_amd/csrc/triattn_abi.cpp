@@ -9,7 +9,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include "../../include/aaq.h"
 #include "../../include/triattn.h"
+#include "aaq_kernels.h"
 #include "triattn_kernels.h"
 
 namespace {
@@ -278,6 +280,32 @@ int triangle_attn_project(const ta_problem* prob, int variant, const ta_weights*
   triattn::ProjectArgs a = project_args(prob, variant, w, z, ws, l);
   if ((rc = enqueue(triattn::launch_project(a, prob->dtype, (hipStream_t)stream)))) return rc;
   if (variant == TA_ROWS) return TA_OK;  // the row block's bias arrives with the attention stage
+  return pack_bias(prob, variant, nullptr, ws, l, (hipStream_t)stream);
+}
+
+int triangle_attn_project_aaq(const ta_problem* prob, int variant, const ta_weights* w, const void* records,
+                              int group, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_problem(prob, variant);
+  if (rc) return rc;
+  if (prob->dtype != TA_BF16) return TA_ERR_BAD_DTYPE;
+  const int rb = aaq::record_bytes(group);
+  if (rb < 0) return TA_ERR_BAD_GROUP;
+  if ((rc = check_weights(w))) return rc;
+  if (records == nullptr || ws == nullptr) return TA_ERR_NULL_PTR;
+  if (!aligned16(records) || !aligned16(ws)) return TA_ERR_MISALIGNED;
+  ta_ws_layout l;
+  layout_of(prob, variant, &l);
+  if (ws_bytes < l.total) return TA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t rec_bytes = (size_t)prob->rows * prob->I * rb;
+  if ((rc = check_out_alias(prob, w, {ws, l.total}, {records, rec_bytes}, {nullptr, 0}, {nullptr, 0}))) return rc;
+  if (overlap({ws, l.total}, {records, rec_bytes})) return TA_ERR_ALIAS;
+  (void)hipGetLastError();
+  triattn::ProjectArgs a = project_args(prob, variant, w, records, ws, l);
+  a.zfmt = group + 1;
+  a.z_line_stride /= kCz;  // in records
+  a.z_pos_stride /= kCz;
+  if ((rc = enqueue(triattn::launch_project(a, prob->dtype, (hipStream_t)stream)))) return rc;
+  if (variant == TA_ROWS) return TA_OK;
   return pack_bias(prob, variant, nullptr, ws, l, (hipStream_t)stream);
 }
 

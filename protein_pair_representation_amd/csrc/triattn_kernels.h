@@ -20,6 +20,9 @@ struct ProjectArgs {
   int bias_row0;          // bias row of line 0
   int I, P, lines;
   int bias_only;
+  // 0: z holds tokens of the compute dtype (strides in elements); 1, 2, 3: z holds
+  // token-wise quantized records of group A, B, C (strides in records; bf16 only)
+  int zfmt;
 };
 
 // K2: fused attention over `lines` lines of `I` keys; P (the padded position

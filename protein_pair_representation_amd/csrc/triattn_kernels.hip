@@ -175,6 +175,80 @@ __device__ __forceinline__ typename El<T>::frag lds_frag(const u32x4* base, int 
   return f;
 }
 
+// ---------------------------------------------------------------- quantized tokens
+// Records of the token-wise quantization of the pair tensor (LightNobel article,
+// section 2.2; layout of include/aaq.h): group A = 128 INT8 codes + 32 B of
+// metadata (160 B), group B = 128 INT4 codes + the same metadata (96 B), group
+// C = 128 INT4 codes + f32 s, u8 z (80 B).  A value is s (q - z) in fp32; in A and
+// B up to 5 outliers (INT16 q_o with scale s_o, channel in the metadata) replace
+// their channel's value (whose code is z, i.e. 0).
+template <int ZF> struct ZRec;
+template <> struct ZRec<1> { static constexpr int RB = 160, CB = 128, BITS = 8; static constexpr bool OUTL = true; };
+template <> struct ZRec<2> { static constexpr int RB = 96, CB = 64, BITS = 4; static constexpr bool OUTL = true; };
+template <> struct ZRec<3> { static constexpr int RB = 80, CB = 64, BITS = 4; static constexpr bool OUTL = false; };
+
+// One lane's half token: channels 16c + 8hh + t (c, t = 0..7).  cw[c] holds their
+// codes (8 bytes for INT8, 4 for INT4); m0, m1 the 32 B of metadata (m1 unused
+// for group C).
+template <int ZF> struct ZHalf {
+  uint32_t cw[8][ZRec<ZF>::BITS == 8 ? 2 : 1];
+  u32x4 m0, m1;
+};
+
+template <int ZF>
+__device__ __forceinline__ void zhalf_load(ZHalf<ZF>& zh, const __attribute__((address_space(1))) uint8_t* rec,
+                                           int hh) {
+  typedef ZRec<ZF> R;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    if (R::BITS == 8) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 w = *reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(rec + 16 * c + 8 * hh);
+      zh.cw[c][0] = w[0];
+      zh.cw[c][R::BITS == 8 ? 1 : 0] = w[1];
+    } else {
+      zh.cw[c][0] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(rec + 8 * c + 4 * hh);
+    }
+  }
+  zh.m0 = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(rec + R::CB);
+  if (R::OUTL) zh.m1 = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(rec + R::CB + 16);
+  else zh.m1 = u32x4{0u, 0u, 0u, 0u};
+}
+
+template <int ZF>
+__device__ __forceinline__ void zhalf_decode(const ZHalf<ZF>& zh, int hh, float (&v)[8][8]) {
+  typedef ZRec<ZF> R;
+  const float s = __uint_as_float(zh.m0[0]);
+  const int z = R::OUTL ? (int)(zh.m1[1] >> 24) : (int)(zh.m0[1] & 0xFFu);
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int q = R::BITS == 8 ? (int)((zh.cw[c][t >> 2] >> (8 * (t & 3))) & 0xFFu)
+                                 : (int)((zh.cw[c][0] >> (4 * t)) & 0xFu);
+      v[c][t] = (float)(q - z) * s;
+    }
+  if (R::OUTL) {
+    const int nst = (int)(zh.m1[2] & 0xFFu);
+    const int n = nst < 5 ? nst : 5;
+    const float s_o = __uint_as_float(zh.m0[1]);
+    for (int k = 0; k < n; ++k) {
+      const uint32_t qw = k < 2 ? zh.m0[2] : (k < 4 ? zh.m0[3] : zh.m1[0]);
+      const int qo = (int)(int16_t)((qw >> (16 * (k & 1))) & 0xFFFFu);
+      const int ch = k < 2 ? (int)((zh.m1[0] >> (16 + 8 * k)) & 0xFFu) : (int)((zh.m1[1] >> (8 * (k - 2))) & 0xFFu);
+      const float val = (float)qo * s_o;
+      if (((ch >> 3) & 1) == hh) {
+        const int c8 = ch >> 4, tt = ch & 7;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (c == c8 && t == tt) v[c][t] = val;
+      }
+    }
+  }
+}
+
 // ================================================================ K1: LN + projections
 // A workgroup of WAVES waves loops over tiles of 32*WAVES tokens (one line,
 // consecutive positions); each wave owns 32 of them.  Lane l holds token
@@ -211,9 +285,13 @@ __device__ __forceinline__ typename El<T>::frag proj_wfrag(const u32x4* w_lds, c
 
 // NT output tiles mt0 .. mt0+NT-1 of one wave's 32 tokens.  SWAP puts the tokens
 // on the A side (rows), which yields the transposed tile (v^T).
+// bf16: the LayerNorm output enters as two bf16 parts, x = hi + lo (lo = the
+// rounding residual of hi), each multiplied by the weights, so the products see x
+// to about 2^-17 instead of bf16's 2^-9 (fp32: xl is unused).
 template <typename T, int WUNITS, int NT, bool SWAP>
 __device__ __forceinline__ void proj_tiles(const u32x4* w_lds, const T* const* wsrc, int mt0, int r, int hh,
-                                           const typename El<T>::frag* xf, f32x16* acc) {
+                                           const typename El<T>::frag* xf, const typename El<T>::frag* xl,
+                                           f32x16* acc) {
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x16{};
 #pragma unroll
@@ -223,6 +301,10 @@ __device__ __forceinline__ void proj_tiles(const u32x4* w_lds, const T* const* w
     for (int j = 0; j < NT; ++j) wf[j] = proj_wfrag<T, WUNITS>(w_lds, wsrc, mt0 + j, r, hh, c);
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = SWAP ? mma(xf[c], wf[j], acc[j]) : mma(wf[j], xf[c], acc[j]);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = SWAP ? mma(xl[c], wf[j], acc[j]) : mma(wf[j], xl[c], acc[j]);
+    }
   }
 }
 
@@ -261,8 +343,9 @@ __device__ __forceinline__ void stage_store(u32x4* buf, int row, int hh, int lan
 // bias (row blocks, whose bias comes from the caller); or the bias alone.
 enum { PROJ_ALL = 0, PROJ_NO_BIAS = 1, PROJ_BIAS_ONLY = 2 };
 
-template <typename T, int MODE>
+template <typename T, int MODE, int ZF = 0>
 __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArgs a) {
+  static_assert(ZF == 0 || sizeof(T) == 2, "quantized tokens feed the bf16 path");
   constexpr int WAVES = ProjCfg<T>::WAVES;
   constexpr bool W_IN_LDS = ProjCfg<T>::W_IN_LDS;
   constexpr int TP = 32 * WAVES;                   // positions per tile (divides P)
@@ -311,14 +394,29 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
   // stores: a value live across the whole iteration cannot share registers with
   // store data, so the loads never wait for earlier stores to release them.
   typedef const __attribute__((address_space(1))) T* gptr;
+  typedef const __attribute__((address_space(1))) uint8_t* rptr;
+  // record of this lane's token (quantized tokens): same clamping as z_addr
+  auto r_addr = [&](int t) {
+    t = t < ntiles ? t : ntiles - 1;
+    const int line = t / pblocks;
+    const int pos = (t - line * pblocks) * TP + wave * 32 + rho(lr);
+    const int pc = pos < I1 ? pos : I1;
+    return (const uint8_t*)a.z + ((size_t)line * a.z_line_stride + (size_t)pc * a.z_pos_stride) * ZRec<ZF ? ZF : 1>::RB;
+  };
+  auto next_addr = [&](int t) { return ZF ? (uint64_t)r_addr(t) : (uint64_t)z_addr(t); };
   frag zp[8];
+  ZHalf<ZF ? ZF : 1> zq;
   int tile = blockIdx.x;
-  uint64_t zn = (uint64_t)z_addr(tile);
+  uint64_t zn = next_addr(tile);
   if (tile < ntiles) {
+    if constexpr (ZF == 0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) zp[c] = *reinterpret_cast<const __attribute__((address_space(1))) frag*>((gptr)zn + 16 * c);
+      for (int c = 0; c < 8; ++c) zp[c] = *reinterpret_cast<const __attribute__((address_space(1))) frag*>((gptr)zn + 16 * c);
+    } else {
+      zhalf_load<ZF>(zq, (rptr)zn, hh);
+    }
   }
-  zn = (uint64_t)z_addr(tile + gridDim.x);
+  zn = next_addr(tile + gridDim.x);
   // One tile.  The first one is peeled off the loop so that the loop is entered
   // with as many stores in flight as its back edge carries: the wait for the
   // prefetched tokens then never has to cover the previous tile's stores.
@@ -331,53 +429,70 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
     int wr = rho(lr);
     asm volatile("" : "+v"(wr));
     frag zc[8];
+    float zv[ZF ? 8 : 1][8];  // quantized tokens: this lane's half token decoded to fp32
+    if constexpr (ZF == 0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) zc[c] = zp[c];
+      for (int c = 0; c < 8; ++c) zc[c] = zp[c];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)  // (the last tile reloads itself)
-      zp[c] = *reinterpret_cast<const __attribute__((address_space(1))) frag*>((gptr)zn + 16 * c);
-    zn = (uint64_t)z_addr(tile + 2 * gridDim.x);
+      for (int c = 0; c < 8; ++c)  // (the last tile reloads itself)
+        zp[c] = *reinterpret_cast<const __attribute__((address_space(1))) frag*>((gptr)zn + 16 * c);
+    } else {
+      const ZHalf<ZF> zcur = zq;
+      zhalf_load<ZF>(zq, (rptr)zn, hh);
+      zhalf_decode<ZF>(zcur, hh, zv);
+    }
+    zn = next_addr(tile + 2 * gridDim.x);
     asm volatile("" : "+v"(zn));
+    auto zval = [&](int c, int t) -> float {
+      if constexpr (ZF == 0) return (float)zc[c][t];
+      else return zv[c][t];
+    };
 
     // ---- LayerNorm: mean, then the centred second moment, then scale and shift
     float s = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) s += (float)zc[c][t];
+      for (int t = 0; t < 8; ++t) s += zval(c, t);
     const float mean = xhalf_sum(s) * (1.0f / CZ);
     float v2 = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float d = (float)zc[c][t] - mean;
+        const float d = zval(c, t) - mean;
         v2 += d * d;
       }
     const float rstd = rsqrtf(xhalf_sum(v2) * (1.0f / CZ) + a.eps);
-    frag xf[8];
+    frag xf[8], xl[sizeof(T) == 2 ? 8 : 1];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const f32x8 gm = *reinterpret_cast<const f32x8*>(par_lds + 16 * c + 8 * hh);
       const f32x8 bt = *reinterpret_cast<const f32x8*>(par_lds + CZ + 16 * c + 8 * hh);
       float t8[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) t8[t] = ((float)zc[c][t] - mean) * rstd * gm[t] + bt[t];
+      for (int t = 0; t < 8; ++t) t8[t] = (zval(c, t) - mean) * rstd * gm[t] + bt[t];
       xf[c] = to_frag<T>(t8);
+      if constexpr (sizeof(T) == 2) {
+        float r8[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) r8[t] = t8[t] - (float)xf[c][t];
+        xl[c] = to_frag<T>(r8);
+      }
     }
 
     f32x16 acc[4];
     float o[16];
     if (MODE != PROJ_BIAS_ONLY) {
       // q (times log2(e)/sqrt(d)) and k: lane = token pos, channels 16*hh + i of head h
-      proj_tiles<T, WUNITS, 4, false>(w_lds, wsrc, 0, wr, hh, xf, acc);
+      proj_tiles<T, WUNITS, 4, false>(w_lds, wsrc, 0, wr, hh, xf, xl, acc);
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[i] = acc[h][i] * (LOG2E * 0.17677669529663687f);
         stage_store<T>(st_buf, rho(lr), hh, lane, o, (T*)a.q + (((size_t)line * NH + h) * a.P + pos0) * HD, HD);
       }
-      proj_tiles<T, WUNITS, 4, false>(w_lds, wsrc, 4, wr, hh, xf, acc);
+      proj_tiles<T, WUNITS, 4, false>(w_lds, wsrc, 4, wr, hh, xf, xl, acc);
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
 #pragma unroll
@@ -385,7 +500,7 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
         stage_store<T>(st_buf, rho(lr), hh, lane, o, (T*)a.k + (((size_t)line * NH + h) * a.P + pos0) * HD, HD);
       }
       // v^T: lane = channel rho(lr) of head h, tokens pos0 + 16*hh + i
-      proj_tiles<T, WUNITS, 4, true>(w_lds, wsrc, 8, wr, hh, xf, acc);
+      proj_tiles<T, WUNITS, 4, true>(w_lds, wsrc, 8, wr, hh, xf, xl, acc);
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
 #pragma unroll
@@ -393,7 +508,7 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
         stage_store<T>(st_buf, rho(lr), hh, lane, o, (T*)a.vt + ((size_t)line * NH + h) * HD * a.P + pos0, a.P);
       }
       // gate after the sigmoid
-      proj_tiles<T, WUNITS, 4, false>(w_lds, wsrc, 12, wr, hh, xf, acc);
+      proj_tiles<T, WUNITS, 4, false>(w_lds, wsrc, 12, wr, hh, xf, xl, acc);
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         const f32x16 bg = *reinterpret_cast<const f32x16*>(par_lds + 2 * CZ + h * HD + 16 * hh);
@@ -407,7 +522,7 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
       // One buffer resource per head spans exactly this line's I entries, so
       // the upper half (pushed past the end) and positions >= I are dropped by
       // the hardware range check instead of a branch.
-      proj_tiles<T, WUNITS, 1, false>(w_lds, wsrc, 16, wr, hh, xf, acc);
+      proj_tiles<T, WUNITS, 1, false>(w_lds, wsrc, 16, wr, hh, xf, xl, acc);
       const int boff = (pos + hh * a.I) * 4;
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
@@ -886,7 +1001,16 @@ hipError_t launch_project(const ProjectArgs& a, int dtype, hipStream_t stream) {
   if (grid < 1) grid = 1;
   const int mode = a.bias_only ? PROJ_BIAS_ONLY : a.bias != nullptr ? PROJ_ALL : PROJ_NO_BIAS;
   const dim3 g((unsigned)grid), b(64 * waves);
-  if (dtype == 1) {
+  if (dtype == 1 && a.zfmt != 0) {
+#define TRIATTN_LAUNCH_Q(ZF)                                                                              \
+  if (mode == PROJ_ALL) hipLaunchKernelGGL((tri_project<__bf16, PROJ_ALL, ZF>), g, b, 0, stream, a);      \
+  else if (mode == PROJ_NO_BIAS) hipLaunchKernelGGL((tri_project<__bf16, PROJ_NO_BIAS, ZF>), g, b, 0, stream, a); \
+  else hipLaunchKernelGGL((tri_project<__bf16, PROJ_BIAS_ONLY, ZF>), g, b, 0, stream, a);
+    if (a.zfmt == 1) { TRIATTN_LAUNCH_Q(1) }
+    else if (a.zfmt == 2) { TRIATTN_LAUNCH_Q(2) }
+    else { TRIATTN_LAUNCH_Q(3) }
+#undef TRIATTN_LAUNCH_Q
+  } else if (dtype == 1) {
     if (mode == PROJ_ALL) hipLaunchKernelGGL((tri_project<__bf16, PROJ_ALL>), g, b, 0, stream, a);
     else if (mode == PROJ_NO_BIAS) hipLaunchKernelGGL((tri_project<__bf16, PROJ_NO_BIAS>), g, b, 0, stream, a);
     else hipLaunchKernelGGL((tri_project<__bf16, PROJ_BIAS_ONLY>), g, b, 0, stream, a);

@@ -85,6 +85,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "triangle_attn_attend_block": ([P, i32, W, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, sz,
                                         vp], i32),
         "triangle_attn_attend_finalize": ([P, i32, W, vp, vp, vp, sz, vp], i32),
+        "triangle_attn_project_aaq": ([P, i32, W, vp, i32, vp, sz, vp], i32),
         "aaq_record_bytes": ([i32], i32),
         "aaq_encode": ([vp, i32, ctypes.c_int64, i32, vp, vp], i32),
         "aaq_decode": ([vp, i32, ctypes.c_int64, vp, i32, vp], i32),
@@ -218,6 +219,19 @@ def triangle_attn_project(z, weights, variant="start", ws=None, stream=None, eps
         ctypes.byref(problem(I, R, z.dtype, eps)), VARIANTS[variant],
         ctypes.byref(weights_struct(weights, z.dtype)), _ptr(z), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+    return ws
+
+
+def triangle_attn_project_aaq(records, weights, I, rows, group, variant="start", ws=None, stream=None, eps=1e-5):
+    """Stage 1 from token-wise quantized records [rows * I, record bytes] (uint8, GPU)
+    of group "A", "B" or "C"; bf16 workspace (returned)."""
+    _dev(records, "records", torch.uint8)
+    code = {"A": 0, "B": 1, "C": 2}.get(group, group)
+    ws = workspace(I, rows, torch.bfloat16, variant, records.device) if ws is None else _dev(ws, "ws")
+    _check(load_library().triangle_attn_project_aaq(
+        ctypes.byref(problem(I, rows, torch.bfloat16, eps)), VARIANTS[variant],
+        ctypes.byref(weights_struct(weights, torch.bfloat16)), _ptr(records), int(code), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
     return ws
 
 

@@ -40,7 +40,7 @@ def layout(lib, p, variant):
 
 def test_exports_match_header(lib):
     names = ta.header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
 
@@ -238,3 +238,20 @@ def test_aaq_record_bytes(lib):
 def test_aaq_rejects(lib, x, dtype, n, group, rec, code):
     assert lib.aaq_encode(x, dtype, n, group, rec, None) == code
     assert lib.aaq_decode(rec, group, n, x, dtype, None) == code
+
+
+def test_project_aaq_rejects(lib):
+    W = ctypes.byref(weights())
+    ws = A + 1024 * MB
+    p = prob(I=64)
+    rec = A + 512 * MB
+    lay = ta.TaWsLayout()
+    assert lib.triangle_attn_workspace_layout(ctypes.byref(p), ta.TA_START, ctypes.byref(lay)) == 0
+    f = lib.triangle_attn_project_aaq
+    assert f(ctypes.byref(prob(I=64, dtype=ta.TA_F32)), ta.TA_START, W, rec, 0, ws, lay.total, None) == -4
+    assert f(ctypes.byref(p), ta.TA_START, W, rec, 3, ws, lay.total, None) == -11
+    assert f(ctypes.byref(p), ta.TA_START, W, None, 0, ws, lay.total, None) == -1
+    assert f(ctypes.byref(p), ta.TA_START, W, rec + 8, 0, ws, lay.total, None) == -6
+    assert f(ctypes.byref(p), ta.TA_START, W, rec, 0, ws, lay.total - 16, None) == -5
+    assert f(ctypes.byref(p), ta.TA_START, W, ws + 4096, 0, ws, lay.total, None) == -7   # records inside ws
+    assert f(ctypes.byref(p), 7, W, rec, 0, ws, lay.total, None) == -9

@@ -30,10 +30,11 @@ def check(gpu, want, dtype, what=""):
     assert got.shape == want.shape, (got.shape, want.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - want)
+    rel = err.sum() / max(np.abs(want).sum(), 1e-300)
+    say(f"    {what}: max abs {err.max():.3e}, rel L1 {rel:.3e}")
     if dtype == "f32":
         assert err.max() <= F32_MAX_ABS, f"{what}: max abs {err.max():.3e}"
     else:
-        rel = err.sum() / max(np.abs(want).sum(), 1e-300)
         assert err.max() <= BF16_MAX_ABS and rel <= BF16_REL_L1, f"{what}: max abs {err.max():.3e}, rel L1 {rel:.3e}"
     return float(err.max())
 
