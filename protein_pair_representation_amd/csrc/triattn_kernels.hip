@@ -650,32 +650,42 @@ __device__ __forceinline__ void map_block(int bid, int n_lg, int nqb, int& lg, i
 
 // Output projection of a workgroup's rows: out^T[c][j] = sum_(h,e) W_o[c][h*32+e]
 // o^T[h*32+e][j] + b_o[c], from the gated head outputs in the workspace (this lane
-// reads back exactly the o values it wrote).
-template <typename T, int ROWS>
-__device__ __forceinline__ void out_projection(const AttendArgs& a, int line0, int j, int hh, int lr) {
+// reads back exactly the o values it wrote).  W_o is first staged into w_lds
+// (the K/V staging area, free once the key loop is over), so that the products
+// run back to back on register and LDS operands.
+template <typename T, int ROWS, int NT>
+__device__ __forceinline__ void out_projection(const AttendArgs& a, int line0, int j, int hh, int lr, u32x4* w_lds) {
   typedef typename El<T>::frag frag;
+  constexpr int WU = CZ * El<T>::bytes / 16;       // 16-B units per W_o row
   const int I = a.I, P = a.P;
   const size_t tok_line = (size_t)NH * P * HD;
+  __syncthreads();                                 // every wave is done with the K/V tiles
+  for (int idx = threadIdx.x; idx < CZ * WU; idx += NT) {
+    const int r = idx / WU, u = idx % WU;
+    lds_put<WU>(w_lds, r, u, reinterpret_cast<const u32x4*>((const T*)a.w_o + (size_t)r * CZ)[u]);
+  }
+  __syncthreads();
 #pragma unroll 1
   for (int r = 0; r < ROWS; ++r) {
     if (line0 + r >= a.lines) break;
     const int line = line0 + r;
     const T* orow_ws = (const T*)a.o + (size_t)line * tok_line + (size_t)j * HD + 16 * hh;
     T* orow = (T*)a.out + (a.out_transposed ? ((size_t)j * I + line) : ((size_t)line * I + j)) * CZ;
+    frag of[NH][2];
+#pragma unroll
+    for (int hd = 0; hd < NH; ++hd)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) of[hd][c] = gld8<T>(orow_ws + (size_t)hd * P * HD + 8 * c);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = a.b_o ? a.b_o[32 * ct + 16 * hh + i] : 0.f;
-      const T* wrow = (const T*)a.w_o + (size_t)(32 * ct + rho(lr)) * CZ + 16 * hh;
 #pragma unroll
       for (int hd = 0; hd < NH; ++hd)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          frag wf = gld8<T>(wrow + 32 * hd + 8 * c);   // W_o is small and stays in L2
-          frag of = gld8<T>(orow_ws + (size_t)hd * P * HD + 8 * c);
-          acc = mma(wf, of, acc);
-        }
+        for (int c = 0; c < 2; ++c)
+          acc = mma(lds_frag<T, WU>(w_lds, 32 * ct + rho(lr), 4 * hd + 2 * hh + c), of[hd][c], acc);
       if (j < I) {
         float ov[16];
 #pragma unroll
@@ -945,7 +955,8 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
     }
   }
 
-  if (!a.state_out) out_projection<T, ROWS>(a, line0, j, hh, lr);
+  static_assert(2 * STAGE_UNITS >= CZ * CZ * El<T>::bytes / 16, "W_o must fit in the K/V staging area");
+  if (!a.state_out) out_projection<T, ROWS, NT>(a, line0, j, hh, lr, &kv_lds[0][0]);
 }
 
 // Bias pack: natural-log fp32 bias [H][I][I] (from K1 or the caller) into the
