@@ -335,7 +335,8 @@ __device__ __forceinline__ void stage_store(u32x4* buf, int row, int hh, int lan
   for (int i = 0; i < LU; ++i) {
     const int U = 64 * i + lane, r = U / RU, uu = U % RU;
     const u32x4 v = buf[r * RU + (uu ^ stage_swz<T>(r))];
-    *reinterpret_cast<u32x4*>(gbase + r * gstride + uu * EPU) = v;
+    // streamed: the attention stage reads these blocks long after they leave
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(gbase + r * gstride + uu * EPU));
   }
 }
 
