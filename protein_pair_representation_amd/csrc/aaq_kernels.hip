@@ -64,8 +64,10 @@ template <> struct Fmt<2> { static constexpr int BITS = 4, RB = 80, CB = 64; sta
 // DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror.
 constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HMIRROR = 0x141;
 
+// Every source lane of these permutes exists, so bound_ctrl is set and no old
+// value needs to be materialised.
 template <int CTRL> __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(uint32_t, v)));
@@ -125,32 +127,26 @@ template <> __device__ __forceinline__ u32x4 pack<float>(const float* v) {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// Store the E codes of one chunk into the staged record (LDS).
-template <int BITS, int E> __device__ __forceinline__ void put_codes(uint8_t* recp, int c0, const int* q) {
+// Store the E codes of one chunk (integral floats in [0, 2^BITS - 1]) into the
+// staged record (LDS).
+template <int BITS, int E> __device__ __forceinline__ void put_codes(uint8_t* recp, int c0, const float* q) {
   if (BITS == 8) {
-    if (E == 8) {
-      uint64_t w = 0;
+    uint32_t w[E / 4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w |= (uint64_t)q[e] << (8 * e);
-      *reinterpret_cast<uint64_t*>(recp + c0) = w;
-    } else {
-      uint32_t w = 0;
+    for (int i = 0; i < E / 4; ++i) {
+      uint32_t a = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w |= (uint32_t)q[e] << (8 * e);
-      *reinterpret_cast<uint32_t*>(recp + c0) = w;
+      for (int e = 0; e < 4; ++e) a = __builtin_amdgcn_cvt_pk_u8_f32(q[4 * i + e], e, a);
+      w[i] = a;
     }
+    if (E == 8) *reinterpret_cast<uint64_t*>(recp + c0) = (uint64_t)w[0] | ((uint64_t)w[E / 4 - 1] << 32);
+    else *reinterpret_cast<uint32_t*>(recp + c0) = w[0];
   } else {
-    if (E == 8) {
-      uint32_t w = 0;
+    uint32_t w = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w |= (uint32_t)q[e] << (4 * e);
-      *reinterpret_cast<uint32_t*>(recp + c0 / 2) = w;
-    } else {
-      uint32_t w = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w |= (uint32_t)q[e] << (4 * e);
-      *reinterpret_cast<uint16_t*>(recp + c0 / 2) = (uint16_t)w;
-    }
+    for (int e = 0; e < E; ++e) w |= (uint32_t)q[e] << (4 * e);
+    if (E == 8) *reinterpret_cast<uint32_t*>(recp + c0 / 2) = w;
+    else *reinterpret_cast<uint16_t*>(recp + c0 / 2) = (uint16_t)w;
   }
 }
 
@@ -211,9 +207,9 @@ __device__ __forceinline__ void encode_body(const T* __restrict__ x, int64_t n, 
       }
       s2 = octet(s2, [](double a, double b) { return a + b; });
       const double lim = 3.0 * __builtin_sqrt(s2 / 128.0);
-      uint32_t fl = 0;
+      uint32_t fl = 0;  // bit j: value j is flagged (built from the top bit down: fl = 2 fl + flag)
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) fl |= (__builtin_fabs(d[j]) > lim ? 1u : 0u) << j;
+      for (int j = VPL - 1; j >= 0; --j) fl = fl + fl + (__builtin_fabs(d[j]) > lim ? 1u : 0u);
 
       uint32_t outm = 0;  // bit j: value j of this lane is a confirmed outlier
       if (__ballot(fl != 0) != 0) {
@@ -315,10 +311,10 @@ __device__ __forceinline__ void encode_body(const T* __restrict__ x, int64_t n, 
     const int z = (int)zf;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-      int q[E];
+      float q[E];
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        q[e] = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(v[k * E + e] * inv) + zf, 0.0f, (float)QMAX);
+        q[e] = __builtin_amdgcn_fmed3f(__builtin_rintf(v[k * E + e] * inv) + zf, 0.0f, (float)QMAX);
       put_codes<F::BITS, E>(mine, chan<T>(k * E, u), q);
     }
 
