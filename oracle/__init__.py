@@ -8,9 +8,10 @@ does, and this package imports nothing from the library.
 * ``oracle.ref``   -- vectorised NumPy float64, materialises the full softmax.
 * ``oracle.brute`` -- pure-Python scalar loops for tiny inputs.
 * ``oracle.aaq``   -- the token-wise quantization codec (records, decode).
+* ``oracle.knn``   -- the k-nearest-neighbour sparse atom-pair encoder.
 
-Parity status: every function here is pinned by ``tests/test_oracle.py`` and
-``tests/test_oracle_aaq.py``
+Parity status: every function here is pinned by ``tests/test_oracle.py``,
+``tests/test_oracle_aaq.py`` and ``tests/test_oracle_knn.py``
 (brute force, torch CPU library routines, closed forms, invariants, and a
 hand-derived golden case under ``tests/golden/``).  No function is
 "parity unpinned".

@@ -191,6 +191,37 @@ def make_tokens(seed: int, n: int, dtype: str = "bf16", c_z: int = C_Z) -> torch
     return torch.from_numpy(out.astype(np.float32)).to(DTYPES[dtype]).contiguous()
 
 
+ATOMS_PER_RESIDUE = 8
+KNN_WORKLOADS = {
+    "knn-L16384-k32": dict(L=16384, k=32, seed=6,
+                           notes="16384 atoms (2048 residues x 8) along a random-walk chain, k = 32"),
+}
+
+
+def make_atoms(seed: int, L: int, c_s: int = 128, c_p: int = 16) -> dict:
+    """Synthetic atoms for the kNN pair encoder: coordinates x [L][3] fp32, single
+    features s [L][c_s] bf16, weights w_l, w_m [c_p][c_s] bf16 (N(0, 1/c_s)),
+    w_d [c_p][4] fp32 (N(0, 1/4)).
+
+    Coordinates: residues along a random walk of 3.8 A steps in uniformly random
+    directions (a chain of alpha carbons), each carrying ATOMS_PER_RESIDUE atoms at
+    N(0, 1.2 A) offsets from it per axis; L is cut from that chain.
+    """
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 13]))
+    n_res = (L + ATOMS_PER_RESIDUE - 1) // ATOMS_PER_RESIDUE
+    steps = rng.standard_normal((n_res, 3))
+    steps *= 3.8 / np.linalg.norm(steps, axis=1, keepdims=True)
+    ca = np.cumsum(steps, axis=0)
+    x = (np.repeat(ca, ATOMS_PER_RESIDUE, axis=0)[:L]
+         + rng.standard_normal((n_res * ATOMS_PER_RESIDUE, 3))[:L] * 1.2).astype(np.float32)
+    s = torch.from_numpy(rng.standard_normal((L, c_s)).astype(np.float32)).to(torch.bfloat16)
+    w_l = torch.from_numpy(rng.standard_normal((c_p, c_s)) / np.sqrt(c_s)).to(torch.bfloat16)
+    w_m = torch.from_numpy(rng.standard_normal((c_p, c_s)) / np.sqrt(c_s)).to(torch.bfloat16)
+    w_d = torch.from_numpy((rng.standard_normal((c_p, 4)) * 0.5).astype(np.float32))
+    return {"x": torch.from_numpy(x), "s": s.contiguous(), "w_l": w_l.contiguous(), "w_m": w_m.contiguous(),
+            "w_d": w_d.contiguous()}
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of stored values (bf16/fp32) to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()
