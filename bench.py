@@ -135,6 +135,47 @@ def aaq_project(z, wd, variant, stream, reps=20):
     return out
 
 
+KNN_SRC = os.path.join(ROOT, "protein_pair_representation_amd", "csrc", "knn_kernels.hip")
+
+
+def knn_bytes(L, k):
+    """Algorithmic HBM bytes of one kNN encode: read coordinates (12 B) and single features
+    (256 B) once per atom, write k neighbour indices (4 B) and k pair rows (32 B)."""
+    return L * (12 + 256 + k * (4 + 32))
+
+
+def knn_encoder(stream, reps=20, name="knn-L16384-k32"):
+    """The kNN sparse pair encoder on its workload (atoms along a chain), timed over `reps`
+    calls (three launches each) with HIP events on `stream`."""
+    import torch
+    from protein_pair_representation_amd import inputs
+    from protein_pair_representation_amd import knn
+    wl = inputs.KNN_WORKLOADS[name]
+    L, k = wl["L"], wl["k"]
+    a = {n_: t.cuda() for n_, t in inputs.make_atoms(wl["seed"], L).items()}
+    nbr = torch.empty((L, k), dtype=torch.int32, device="cuda")
+    pair = torch.empty((L, k, 16), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(knn.knn_workspace_bytes(L), dtype=torch.uint8, device="cuda")
+
+    def launch():
+        knn.knn_pair_encode(a["x"], a["s"], k, a["w_l"], a["w_m"], a["w_d"], nbr=nbr, pair=pair, ws=ws,
+                            stream=stream)
+    launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nb = knn_bytes(L, k)
+    return {"workload": name, "atoms": L, "k": k, "avg_call_ms": round(ms, 4),
+            "pairs_per_s": round(L * k / (ms * 1e-3), 1), "algorithmic_bytes": nb,
+            "GB/s": round(nb / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "kernel_sha": kernel_sha(KNN_SRC)}
+
+
 def read_traffic(workload):
     """HBM bytes per tri_attend launch from the committed rocprofv3 --pmc summary, if current."""
     path = os.path.join(PROFILE_DIR, f"tri_attend_{workload}_pmc.txt")
@@ -261,7 +302,7 @@ def _short(name):
     for key in ("tri_attend", "tri_project", "tri_pack_bias", "copyBuffer"):
         if key in name:
             return key
-    m = re.search(r"aaq_(encode|decode)_([ABC])_(bf16|f32)", name)
+    m = re.search(r"aaq_(encode|decode)_([ABC])_(bf16|f32)|knn_(project|boxes|select_encode)", name)
     if m:
         return m.group(0)
     return name[:60]
@@ -305,7 +346,7 @@ def summarize_pmc(run_dir, workload, copy_mib, family="tri"):
     else:
         wl_path = os.path.join(PROFILE_DIR, f"tri_attend_{workload}_pmc.txt")
         sha = kernel_sha()
-        cmd_b = f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline --key-blocks 0 --aaq 0"
+        cmd_b = f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline --key-blocks 0 --aaq 0 --knn 0"
         tail = [f"traffic_bytes_per_launch={per.get('tri_attend', 0.0):.6e} kernel_sha={sha}",
                 f"tri_project_traffic_bytes_per_launch={per.get('tri_project', 0.0):.6e} kernel_sha={sha}"]
     cmd_c = f"python3 $R/bench.py --copy-calibration {copy_mib}"
@@ -337,9 +378,13 @@ def summarize_trace(run_dir, workload, steps, warmup, family="tri"):
         run = f"python3 $R/bench.py --workload {workload} --aaq-only --steps {steps}"
         summ = f"python3 bench.py --summarize-trace $O/kt --workload {workload} --steps {steps} --family aaq"
         sha, path = kernel_sha(AAQ_SRC), os.path.join(PROFILE_DIR, f"aaq_{workload}_trace.txt")
+    elif family == "knn":
+        run = f"python3 $R/bench.py --knn-only --steps {steps}"
+        summ = f"python3 bench.py --summarize-trace $O/kt --steps {steps} --family knn"
+        sha, path = kernel_sha(KNN_SRC), os.path.join(PROFILE_DIR, "knn_knn-L16384-k32_trace.txt")
     else:
         run = (f"python3 $R/bench.py --workload {workload} --steps {steps} --warmup {warmup} --no-cpu-baseline "
-               f"--key-blocks 0 --aaq 0")
+               f"--key-blocks 0 --aaq 0 --knn 0")
         summ = f"python3 bench.py --summarize-trace $O/kt --workload {workload} --steps {steps} --warmup {warmup}"
         sha, path = kernel_sha(), os.path.join(PROFILE_DIR, f"kernels_{workload}_trace.txt")
     out = [f"# rocprofv3 kernel statistics, workload {workload}, gfx950 (MI355X)",
@@ -377,7 +422,10 @@ def main():
     ap.add_argument("--aaq", type=int, default=1, help="also time the AAQ codec on the pair tensor (0: skip)")
     ap.add_argument("--aaq-only", action="store_true",
                     help="time only the AAQ codec (encode/decode, groups A and B) over --steps launches each")
-    ap.add_argument("--family", default="tri", choices=["tri", "aaq"],
+    ap.add_argument("--knn", type=int, default=1, help="also time the kNN sparse pair encoder (0: skip)")
+    ap.add_argument("--knn-only", action="store_true",
+                    help="time only the kNN sparse pair encoder (knn-L16384-k32) over --steps calls")
+    ap.add_argument("--family", default="tri", choices=["tri", "aaq", "knn"],
                     help="kernel family of --summarize-pmc / --summarize-trace")
     args = ap.parse_args()
     if args.summarize_pmc:
@@ -403,6 +451,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    if args.knn_only:
+        print(json.dumps({"knn": knn_encoder(torch.cuda.current_stream(), reps=args.steps)}), flush=True)
         return
 
     wl = inputs.WORKLOADS[args.workload]
@@ -505,6 +557,8 @@ def main():
         res["aaq"] = aaq_codec(z, wl.name, stream)
         if wl.dtype == "bf16":
             res["aaq"]["project_stage"] = aaq_project(z, wd, variants[0], stream)
+    if args.knn > 0:
+        res["knn"] = knn_encoder(stream)
     if not args.no_cpu_baseline and z_host is not None:
         res["cpu_baseline"] = cpu_baseline(wl, z_host, w_host)
     print(json.dumps(res), flush=True)

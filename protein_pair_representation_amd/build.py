@@ -15,7 +15,9 @@ LIB_PATH = os.path.join(PKG_DIR, "libtriattn.so")
 SOURCES = [os.path.join(PKG_DIR, "csrc", "triattn_kernels.hip"),
            os.path.join(PKG_DIR, "csrc", "triattn_abi.cpp"),
            os.path.join(PKG_DIR, "csrc", "aaq_kernels.hip"),
-           os.path.join(PKG_DIR, "csrc", "aaq_abi.cpp")]
+           os.path.join(PKG_DIR, "csrc", "aaq_abi.cpp"),
+           os.path.join(PKG_DIR, "csrc", "knn_kernels.hip"),
+           os.path.join(PKG_DIR, "csrc", "knn_abi.cpp")]
 ARCH = "gfx950"
 # Packed fp32 instructions are switched off for all device code.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

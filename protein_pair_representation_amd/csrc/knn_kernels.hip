@@ -1,0 +1,268 @@
+// knn_kernels.hip -- k-nearest-neighbour sparse atom-pair encoder on gfx950.
+//
+// What is computed (Design-CP summary, implementation details, memory
+// optimisation: the atom-pair tensor is built on the fly at the sparse indices
+// of each atom's k nearest neighbours, never densely):
+//  * N(l): the k atoms m != l with the smallest squared distance to atom l,
+//    ascending, equal distances to the lower index.  The squared distance is
+//    float32 ((dx*dx + dy*dy) + dz*dz), d = x_l - x_m, with no fused operations,
+//    so the selection is exact and reproducible;
+//  * p_lm = W_l s_l + W_m s_m + W_d (d_x, d_y, d_z, 1 / (1 + |d|^2)) for m in
+//    N(l), c_s = 128 single channels (bf16), c_p = 16 pair channels, stored bf16.
+//
+// Kernels, in launch order:
+//  * knn_project: A = s W_l^T and B = s W_m^T per atom (fp32, [L][2][16]), the
+//    single-feature halves of every pair, computed once per atom;
+//  * knn_boxes: one wave per chunk of 64 consecutive atoms: the coordinates
+//    copied as float4 (one 16-byte load per candidate later) and the chunk's
+//    axis-aligned bounding box;
+//  * knn_select_encode: one wave per query atom.  Lanes 0..k-1 hold the best
+//    list found so far, sorted by (d2, index); lane 63 down to k hold +inf.
+//    Chunks are scanned 64 candidates at a time (one per lane); the few that
+//    beat the k-th entry are inserted one by one: the insert position is the
+//    popcount of a ballot, and the list moves up by a whole-wave DPP shift.
+//    The query's own chunk and its two chain neighbours go first, so the k-th
+//    distance is small early; every other chunk is skipped when the squared
+//    distance from the query to its box exceeds the k-th distance.  That skip
+//    is exact: the box bound is evaluated with the same float32 operations in
+//    the same order as a candidate's distance, and correctly rounded
+//    subtraction, squaring and addition are monotone, so no candidate of a
+//    skipped chunk can round to a value at or below the bound.  Lane n then
+//    builds pair (l, N(l)[n]); the k pairs of a query are one contiguous run
+//    of 32-byte rows.
+// Atoms stored along the chain (consecutive indices close in space, as in a
+// protein) give tight boxes and few scanned chunks; any order gives the same
+// result, only slower.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "knn_kernels.h"
+
+namespace knn {
+namespace {
+
+constexpr int CS = 128;        // single channels
+constexpr int CP = 16;         // pair channels
+constexpr int CH = 64;         // atoms per chunk: one per lane
+constexpr int QPB = 4;         // query waves per workgroup
+constexpr int DPP_WAVE_SHR1 = 0x138;
+constexpr int NO_ATOM = 0x7FFFFFFF;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- single-feature halves
+// One lane per (atom, output channel of A or B): a 128-long dot product, fp32
+// fused multiply-adds over the exact products of bf16 values, channel order.
+__global__ void __launch_bounds__(256) knn_project(const uint16_t* __restrict__ s, const uint16_t* __restrict__ w_l,
+                                                   const uint16_t* __restrict__ w_m, float* __restrict__ ab, int L) {
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int l = gid >> 5, o = gid & 31;             // o < 16: A channel o, else B channel o - 16
+  if (l >= L) return;
+  const u32x4* sr = reinterpret_cast<const u32x4*>(s + (size_t)l * CS);
+  const u32x4* wr = reinterpret_cast<const u32x4*>(o < CP ? w_l + (size_t)o * CS : w_m + (size_t)(o - CP) * CS);
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < CS / 8; ++u) {
+    const u32x4 a = sr[u], b = wr[u];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
+      acc = fmaf(__uint_as_float(a[i] & 0xFFFF0000u), __uint_as_float(b[i] & 0xFFFF0000u), acc);
+    }
+  }
+  ab[(size_t)l * 2 * CP + o] = acc;
+}
+
+// ---------------------------------------------------------------- chunk boxes
+__global__ void __launch_bounds__(CH) knn_boxes(const float* __restrict__ x, int L, float4* __restrict__ xp,
+                                                float4* __restrict__ box) {
+  const int c = blockIdx.x, lane = threadIdx.x;
+  const int m = c * CH + lane;
+  const bool ok = m < L;
+  const float px = ok ? x[3 * (size_t)m] : 0.f, py = ok ? x[3 * (size_t)m + 1] : 0.f,
+              pz = ok ? x[3 * (size_t)m + 2] : 0.f;
+  xp[m] = make_float4(px, py, pz, 0.f);
+  const float inf = __builtin_inff();
+  float lx = ok ? px : inf, ly = ok ? py : inf, lz = ok ? pz : inf;
+  float hx = ok ? px : -inf, hy = ok ? py : -inf, hz = ok ? pz : -inf;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    lx = fminf(lx, __shfl_xor(lx, w));
+    ly = fminf(ly, __shfl_xor(ly, w));
+    lz = fminf(lz, __shfl_xor(lz, w));
+    hx = fmaxf(hx, __shfl_xor(hx, w));
+    hy = fmaxf(hy, __shfl_xor(hy, w));
+    hz = fmaxf(hz, __shfl_xor(hz, w));
+  }
+  if (lane == 0) {
+    box[2 * c] = make_float4(lx, ly, lz, 0.f);
+    box[2 * c + 1] = make_float4(hx, hy, hz, 0.f);
+  }
+}
+
+// ---------------------------------------------------------------- selection + pairs
+__device__ __forceinline__ float sq_dist(float xl, float yl, float zl, float xm, float ym, float zm) {
+#pragma clang fp contract(off)
+  const float dx = xl - xm, dy = yl - ym, dz = zl - zm;
+  return (dx * dx + dy * dy) + dz * dz;
+}
+
+// Lower bound of sq_dist(query, m) over every m in the box: per axis the gap
+// lo - q or q - hi (rounded like the candidate's own difference), else 0.
+__device__ __forceinline__ float box_bound(float xl, float yl, float zl, float4 lo, float4 hi) {
+#pragma clang fp contract(off)
+  const float gx = fmaxf(fmaxf(lo.x - xl, xl - hi.x), 0.f);
+  const float gy = fmaxf(fmaxf(lo.y - yl, yl - hi.y), 0.f);
+  const float gz = fmaxf(fmaxf(lo.z - zl, zl - hi.z), 0.f);
+  return (gx * gx + gy * gy) + gz * gz;
+}
+
+__device__ __forceinline__ float wave_shr1_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), DPP_WAVE_SHR1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ int wave_shr1_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, DPP_WAVE_SHR1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// The best list of one query wave: (bd, bi) per lane, (td, ti) = entry k-1.
+struct Best {
+  float bd, td;
+  int bi, ti;
+};
+
+__device__ __forceinline__ void scan_chunk(const float4* __restrict__ xp, int c, int l, int L, int k, int lane,
+                                           float xl, float yl, float zl, Best& b) {
+  const int m = c * CH + lane;
+  const float4 p = xp[m];                            // padded to whole chunks
+  const bool ok = m < L && m != l;
+  const float d2 = sq_dist(xl, yl, zl, p.x, p.y, p.z);
+  uint64_t mask = __ballot(ok && (d2 < b.td || (d2 == b.td && m < b.ti)));
+  while (mask) {
+    const int src = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    const float cd = readlane_f(d2, src);
+    const int ci = __builtin_amdgcn_readlane(m, src);
+    if (!(cd < b.td || (cd == b.td && ci < b.ti))) continue;   // the k-th entry moved below it
+    // entries ahead of the candidate; the k-th is not, so pos <= k - 1
+    const int pos = __builtin_popcountll(__ballot(b.bd < cd || (b.bd == cd && b.bi < ci)));
+    const float pd = wave_shr1_f(b.bd);
+    const int pi = wave_shr1_i(b.bi);
+    if (lane > pos) {
+      b.bd = pd;
+      b.bi = pi;
+    } else if (lane == pos) {
+      b.bd = cd;
+      b.bi = ci;
+    }
+    if (lane >= k) {                                 // the entry pushed out of the list
+      b.bd = __builtin_inff();
+      b.bi = NO_ATOM;
+    }
+    b.td = readlane_f(b.bd, k - 1);
+    b.ti = __builtin_amdgcn_readlane(b.bi, k - 1);
+  }
+}
+
+__global__ void __launch_bounds__(64 * QPB) knn_select_encode(const float4* __restrict__ xp,
+                                                              const float4* __restrict__ box,
+                                                              const float* __restrict__ ab,
+                                                              const float* __restrict__ w_d, int L, int k,
+                                                              int32_t* __restrict__ nbr,
+                                                              uint16_t* __restrict__ pair) {
+  const int lane = threadIdx.x & 63;
+  const int l = blockIdx.x * QPB + (threadIdx.x >> 6);
+  if (l >= L) return;                                // whole waves leave
+  const float4 q = xp[l];
+  const float xl = q.x, yl = q.y, zl = q.z;
+  Best b{__builtin_inff(), __builtin_inff(), NO_ATOM, NO_ATOM};
+
+  const int nch = (L + CH - 1) / CH;
+  const int c0 = l / CH;
+  scan_chunk(xp, c0, l, L, k, lane, xl, yl, zl, b);
+  if (c0 > 0) scan_chunk(xp, c0 - 1, l, L, k, lane, xl, yl, zl, b);
+  if (c0 + 1 < nch) scan_chunk(xp, c0 + 1, l, L, k, lane, xl, yl, zl, b);
+  for (int g = 0; g < nch; g += 64) {                // 64 boxes tested at once, one per lane
+    const int c = g + lane;
+    const bool fresh = c < nch && (c < c0 - 1 || c > c0 + 1);
+    const float lb = fresh ? box_bound(xl, yl, zl, box[2 * c], box[2 * c + 1]) : __builtin_inff();
+    uint64_t mask = __ballot(fresh && lb <= b.td);
+    while (mask) {
+      const int src = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      if (readlane_f(lb, src) > b.td) continue;      // pruned by a later k-th distance
+      scan_chunk(xp, g + src, l, L, k, lane, xl, yl, zl, b);
+    }
+  }
+
+  if (lane >= k) return;
+  // Every slot is filled when k <= L - 1 and all distances are finite; an
+  // empty one (non-finite coordinates) is reported as -1 with the pair of l itself.
+  const bool have = (unsigned)b.bi < (unsigned)L;
+  const int m = have ? b.bi : l;
+  const float4 pm = xp[m];
+  const float dx = xl - pm.x, dy = yl - pm.y, dz = zl - pm.z;
+  const float ph[4] = {dx, dy, dz, 1.0f / (1.0f + (have ? b.bd : 0.f))};
+  const float4* al = reinterpret_cast<const float4*>(ab + (size_t)l * 2 * CP);
+  const float4* bm = reinterpret_cast<const float4*>(ab + (size_t)m * 2 * CP + CP);
+  float v[CP];
+#pragma unroll
+  for (int u = 0; u < CP / 4; ++u) {
+    const float4 a4 = al[u], b4 = bm[u];
+    v[4 * u] = a4.x + b4.x;
+    v[4 * u + 1] = a4.y + b4.y;
+    v[4 * u + 2] = a4.z + b4.z;
+    v[4 * u + 3] = a4.w + b4.w;
+  }
+  uint32_t packed[CP / 2];
+#pragma unroll
+  for (int o = 0; o < CP; ++o) {
+    float acc = v[o];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = fmaf(w_d[o * 4 + j], ph[j], acc);
+    const uint32_t h = __builtin_bit_cast(uint16_t, (__bf16)acc);
+    packed[o / 2] = (o & 1) ? (packed[o / 2] | (h << 16)) : h;
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(pair + ((size_t)l * k + lane) * CP);
+  dst[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+  dst[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+  nbr[(size_t)l * k + lane] = have ? m : -1;
+}
+
+}  // namespace
+
+WsLayout workspace_layout(int64_t L) {
+  WsLayout w;
+  const int64_t nch = (L + CH - 1) / CH;
+  w.ab = 0;
+  w.xp = (size_t)L * 2 * CP * sizeof(float);
+  w.box = w.xp + (size_t)nch * CH * sizeof(float4);
+  w.total = w.box + (size_t)nch * 2 * sizeof(float4);
+  return w;
+}
+
+hipError_t launch_encode(const float* x, const void* s, int L, int k, const void* w_l, const void* w_m,
+                         const float* w_d, int32_t* nbr, void* pair, void* ws, hipStream_t stream) {
+  if (L <= 0) return hipSuccess;
+  const WsLayout w = workspace_layout(L);
+  char* base = static_cast<char*>(ws);
+  float* ab = reinterpret_cast<float*>(base + w.ab);
+  float4* xp = reinterpret_cast<float4*>(base + w.xp);
+  float4* box = reinterpret_cast<float4*>(base + w.box);
+  const int nch = (L + CH - 1) / CH;
+  hipLaunchKernelGGL(knn_project, dim3((unsigned)(((size_t)L * 32 + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(s), static_cast<const uint16_t*>(w_l),
+                     static_cast<const uint16_t*>(w_m), ab, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(knn_boxes, dim3((unsigned)nch), dim3(CH), 0, stream, x, L, xp, box);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(knn_select_encode, dim3((unsigned)((L + QPB - 1) / QPB)), dim3(64 * QPB), 0, stream, xp, box,
+                     ab, w_d, L, k, nbr, static_cast<uint16_t*>(pair));
+  return hipGetLastError();
+}
+
+}  // namespace knn

@@ -53,11 +53,11 @@ _lib = None
 
 
 def header_functions() -> list:
-    """Names of the functions include/triattn.h and include/aaq.h declare."""
+    """Names of the functions include/triattn.h, aaq.h and knn.h declare."""
     names = set()
-    for h in ("triattn.h", "aaq.h"):
+    for h in ("triattn.h", "aaq.h", "knn.h"):
         text = open(os.path.join(ROOT, "include", h)).read()
-        names |= set(re.findall(r"\b((?:triangle_attn|aaq)_\w+)\s*\(", text))
+        names |= set(re.findall(r"\b((?:triangle_attn|aaq|knn)_\w+)\s*\(", text))
     return sorted(names)
 
 
@@ -89,6 +89,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "aaq_record_bytes": ([i32], i32),
         "aaq_encode": ([vp, i32, ctypes.c_int64, i32, vp, vp], i32),
         "aaq_decode": ([vp, i32, ctypes.c_int64, vp, i32, vp], i32),
+        "knn_workspace_bytes": ([ctypes.c_int64, ctypes.POINTER(sz)], i32),
+        "knn_pair_encode": ([vp, vp, ctypes.c_int64, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

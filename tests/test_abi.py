@@ -40,7 +40,7 @@ def layout(lib, p, variant):
 
 def test_exports_match_header(lib):
     names = ta.header_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
 
@@ -255,3 +255,40 @@ def test_project_aaq_rejects(lib):
     assert f(ctypes.byref(p), ta.TA_START, W, rec, 0, ws, lay.total - 16, None) == -5
     assert f(ctypes.byref(p), ta.TA_START, W, ws + 4096, 0, ws, lay.total, None) == -7   # records inside ws
     assert f(ctypes.byref(p), 7, W, rec, 0, ws, lay.total, None) == -9
+
+
+def test_knn_workspace_bytes(lib):
+    n = ctypes.c_size_t()
+    assert lib.knn_workspace_bytes(16384, ctypes.byref(n)) == 0
+    # A and B halves fp32 [L][32], float4 coordinates per 64-atom chunk, two float4 per chunk
+    assert n.value == 16384 * 128 + 256 * 64 * 16 + 256 * 32
+    assert lib.knn_workspace_bytes(100, ctypes.byref(n)) == 0 and n.value == 100 * 128 + 2 * 64 * 16 + 2 * 32
+    assert lib.knn_workspace_bytes(0, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.knn_workspace_bytes(-1, ctypes.byref(n)) == -2
+    assert lib.knn_workspace_bytes((1 << 24) + 1, ctypes.byref(n)) == -2
+    assert lib.knn_workspace_bytes(10, None) == -1
+
+
+def test_knn_rejects(lib):
+    L, k = 1000, 32
+    n = ctypes.c_size_t()
+    lib.knn_workspace_bytes(L, ctypes.byref(n))
+    args = dict(x=A, s=A + 1 * MB, L=L, k=k, w_l=A + 2 * MB, w_m=A + 3 * MB, w_d=A + 4 * MB,
+                nbr=A + 5 * MB, pair=A + 10 * MB, ws=A + 20 * MB, ws_bytes=n.value)
+
+    def call(**over):
+        a = dict(args, **over)
+        return lib.knn_pair_encode(a["x"], a["s"], a["L"], a["k"], a["w_l"], a["w_m"], a["w_d"], a["nbr"],
+                                   a["pair"], a["ws"], a["ws_bytes"], None)
+
+    assert call(k=0) == -2 and call(k=65) == -2 and call(L=-1) == -2 and call(L=(1 << 24) + 1) == -2
+    assert call(L=1, k=1) == -2 and call(L=32, k=32) == -2
+    assert call(L=0, x=None, s=None) == 0                   # nothing to do, nothing enqueued
+    for name in ("x", "s", "w_l", "w_m", "w_d", "nbr", "pair", "ws"):
+        assert call(**{name: None}) == -1, name
+        assert call(**{name: args[name] + 4}) == -6, name
+    assert call(ws_bytes=n.value - 1) == -5
+    assert call(pair=A + 5 * MB + 256) == -7                 # pair overlaps nbr
+    assert call(nbr=A) == -7                                 # nbr overlaps x
+    assert call(ws=A + 10 * MB + 1024) == -7                 # ws overlaps pair
+    assert call(pair=A + 1 * MB) == -7                       # pair overlaps s
