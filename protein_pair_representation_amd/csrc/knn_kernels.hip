@@ -12,15 +12,17 @@
 //
 // Kernels, in launch order:
 //  * knn_project: A = s W_l^T and B = s W_m^T per atom (fp32, [L][2][16]), the
-//    single-feature halves of every pair, computed once per atom;
+//    single-feature halves of every pair, computed once per atom on MFMA;
 //  * knn_boxes: one wave per chunk of 64 consecutive atoms: the coordinates
 //    copied as float4 (one 16-byte load per candidate later) and the chunk's
 //    axis-aligned bounding box;
 //  * knn_select_encode: one wave per query atom.  Lanes 0..k-1 hold the best
 //    list found so far, sorted by (d2, index); lane 63 down to k hold +inf.
-//    Chunks are scanned 64 candidates at a time (one per lane); the few that
-//    beat the k-th entry are inserted one by one: the insert position is the
-//    popcount of a ballot, and the list moves up by a whole-wave DPP shift.
+//    Chunks are scanned 64 candidates at a time (one per lane).  When many
+//    beat the k-th entry (the first chunks), the chunk is sorted (bitonic,
+//    across lanes) and merged into the list; when few do, they are inserted
+//    one by one: the insert position is the popcount of a ballot, and the
+//    list moves up by a whole-wave DPP shift.
 //    The query's own chunk and its two chain neighbours go first, so the k-th
 //    distance is small early; every other chunk is skipped when the squared
 //    distance from the query to its box exceeds the k-th distance.  That skip
@@ -46,31 +48,43 @@ constexpr int CP = 16;         // pair channels
 constexpr int CH = 64;         // atoms per chunk: one per lane
 constexpr int QPB = 4;         // query waves per workgroup
 constexpr int DPP_WAVE_SHR1 = 0x138;
-constexpr int NO_ATOM = 0x7FFFFFFF;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- single-feature halves
-// One lane per (atom, output channel of A or B): a 128-long dot product, fp32
-// fused multiply-adds over the exact products of bf16 values, channel order.
+// One wave per 32 atoms: [A | B] (32 atoms x 32 channels) = s W^T with
+// W = [W_l; W_m], eight v_mfma_f32_32x32x16_bf16 over the 128 single channels
+// (exact bf16 products, float32 accumulation).  Operand layout: lane q holds
+// row (q & 31) of the 32x16 A-slice and column (q & 31) of the 16x32 B-slice,
+// contraction slots 8 (q >> 5) + t; the result holds in lane q column (q & 31)
+// and rows 8 (i / 4) + 4 (q >> 5) + (i % 4), i = 0..15.  A = W with its rows
+// permuted so that lane q's 16 results are the consecutive channels
+// 16 (q >> 5) + i of atom (q & 31): one 64-byte store per lane.
 __global__ void __launch_bounds__(256) knn_project(const uint16_t* __restrict__ s, const uint16_t* __restrict__ w_l,
                                                    const uint16_t* __restrict__ w_m, float* __restrict__ ab, int L) {
-  const int gid = blockIdx.x * 256 + threadIdx.x;
-  const int l = gid >> 5, o = gid & 31;             // o < 16: A channel o, else B channel o - 16
-  if (l >= L) return;
-  const u32x4* sr = reinterpret_cast<const u32x4*>(s + (size_t)l * CS);
-  const u32x4* wr = reinterpret_cast<const u32x4*>(o < CP ? w_l + (size_t)o * CS : w_m + (size_t)(o - CP) * CS);
-  float acc = 0.f;
+  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
+  const int atom0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 32;
+  if (atom0 >= L) return;
+  const int o = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);     // channel of result row r
+  const uint16_t* wrow = o < CP ? w_l + (size_t)o * CS : w_m + (size_t)(o - CP) * CS;
+  const int atom = atom0 + r;
+  const uint16_t* srow = s + (size_t)(atom < L ? atom : L - 1) * CS;
+  bf16x8 a[CS / 16], b[CS / 16];
 #pragma unroll
-  for (int u = 0; u < CS / 8; ++u) {
-    const u32x4 a = sr[u], b = wr[u];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
-      acc = fmaf(__uint_as_float(a[i] & 0xFFFF0000u), __uint_as_float(b[i] & 0xFFFF0000u), acc);
-    }
+  for (int u = 0; u < CS / 16; ++u) {
+    a[u] = *reinterpret_cast<const bf16x8*>(wrow + 16 * u + 8 * h);
+    b[u] = *reinterpret_cast<const bf16x8*>(srow + 16 * u + 8 * h);
   }
-  ab[(size_t)l * 2 * CP + o] = acc;
+  f32x16 acc = {};
+#pragma unroll
+  for (int u = 0; u < CS / 16; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u], acc, 0, 0, 0);
+  if (atom < L) {
+    float4* dst = reinterpret_cast<float4*>(ab + (size_t)atom * 2 * CP + CP * h);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dst[v] = make_float4(acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]);
+  }
 }
 
 // ---------------------------------------------------------------- chunk boxes
@@ -117,20 +131,62 @@ __device__ __forceinline__ float box_bound(float xl, float yl, float zl, float4 
   return (gx * gx + gy * gy) + gz * gz;
 }
 
-__device__ __forceinline__ float wave_shr1_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), DPP_WAVE_SHR1, 0xF, 0xF, false));
+// A list entry is the 64-bit key (bits of d2) << 32 | index: for d2 >= 0 the
+// float bits order like the values, so keys order by (d2, index).
+typedef unsigned long long u64;
+constexpr u64 EMPTY = 0x7F800000FFFFFFFFull;     // (+inf, no atom)
+constexpr int NINS = 8;                           // at most this many beaters: insert one by one
+
+__device__ __forceinline__ u64 key_of(float d2, int m) { return ((u64)__float_as_uint(d2) << 32) | (uint32_t)m; }
+__device__ __forceinline__ float key_d2(u64 key) { return __uint_as_float((uint32_t)(key >> 32)); }
+
+__device__ __forceinline__ u64 join(uint32_t lo, uint32_t hi) { return ((u64)hi << 32) | lo; }
+__device__ __forceinline__ u64 shfl_xor64(u64 v, int j) {
+  return join((uint32_t)__shfl_xor((int)(uint32_t)v, j), (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), j));
 }
-__device__ __forceinline__ int wave_shr1_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, DPP_WAVE_SHR1, 0xF, 0xF, false);
+__device__ __forceinline__ u64 shfl64(u64 v, int src) {
+  return join((uint32_t)__shfl((int)(uint32_t)v, src), (uint32_t)__shfl((int)(uint32_t)(v >> 32), src));
 }
-__device__ __forceinline__ float readlane_f(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+__device__ __forceinline__ u64 wave_shr1(u64 v) {
+  return join((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, DPP_WAVE_SHR1, 0xF, 0xF, false),
+              (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), DPP_WAVE_SHR1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ u64 readlane64(u64 v, int lane) {
+  return join((uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane),
+              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane));
 }
 
-// The best list of one query wave: (bd, bi) per lane, (td, ti) = entry k-1.
+// Bitonic sort of one key per lane into ascending lane order.
+__device__ __forceinline__ u64 sort64(u64 key, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      const u64 other = shfl_xor64(key, j);
+      const bool keep_min = ((lane & j) == 0) == ((lane & size) == 0);
+      key = keep_min ? (other < key ? other : key) : (other > key ? other : key);
+    }
+  return key;
+}
+
+// The 64 smallest of two ascending lists, ascending: the elementwise minimum of
+// one list and the other reversed is a bitonic sequence holding them; a
+// bitonic merge sorts it.
+__device__ __forceinline__ u64 merge64(u64 list, u64 batch, int lane) {
+  const u64 rev = shfl64(batch, 63 - lane);
+  u64 key = rev < list ? rev : list;
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) {
+    const u64 other = shfl_xor64(key, j);
+    key = (lane & j) == 0 ? (other < key ? other : key) : (other > key ? other : key);
+  }
+  return key;
+}
+
+// The best list of one query wave: one key per lane (lanes >= k hold EMPTY);
+// tk = the key in lane k - 1, the bar a candidate must beat.
 struct Best {
-  float bd, td;
-  int bi, ti;
+  u64 key, tk;
 };
 
 __device__ __forceinline__ void scan_chunk(const float4* __restrict__ xp, int c, int l, int L, int k, int lane,
@@ -138,31 +194,26 @@ __device__ __forceinline__ void scan_chunk(const float4* __restrict__ xp, int c,
   const int m = c * CH + lane;
   const float4 p = xp[m];                            // padded to whole chunks
   const bool ok = m < L && m != l;
-  const float d2 = sq_dist(xl, yl, zl, p.x, p.y, p.z);
-  uint64_t mask = __ballot(ok && (d2 < b.td || (d2 == b.td && m < b.ti)));
-  while (mask) {
+  const u64 ck = key_of(sq_dist(xl, yl, zl, p.x, p.y, p.z), m);
+  const bool beats = ok && ck < b.tk;
+  uint64_t mask = __ballot(beats);
+  if (__builtin_popcountll(mask) > NINS) {           // many: sort the chunk, merge it in
+    const u64 merged = merge64(b.key, sort64(beats ? ck : EMPTY, lane), lane);
+    b.key = lane < k ? merged : EMPTY;
+    b.tk = readlane64(b.key, k - 1);
+    return;
+  }
+  while (mask) {                                     // few: insert one at a time
     const int src = __builtin_ctzll(mask);
     mask &= mask - 1;
-    const float cd = readlane_f(d2, src);
-    const int ci = __builtin_amdgcn_readlane(m, src);
-    if (!(cd < b.td || (cd == b.td && ci < b.ti))) continue;   // the k-th entry moved below it
-    // entries ahead of the candidate; the k-th is not, so pos <= k - 1
-    const int pos = __builtin_popcountll(__ballot(b.bd < cd || (b.bd == cd && b.bi < ci)));
-    const float pd = wave_shr1_f(b.bd);
-    const int pi = wave_shr1_i(b.bi);
-    if (lane > pos) {
-      b.bd = pd;
-      b.bi = pi;
-    } else if (lane == pos) {
-      b.bd = cd;
-      b.bi = ci;
-    }
-    if (lane >= k) {                                 // the entry pushed out of the list
-      b.bd = __builtin_inff();
-      b.bi = NO_ATOM;
-    }
-    b.td = readlane_f(b.bd, k - 1);
-    b.ti = __builtin_amdgcn_readlane(b.bi, k - 1);
+    const u64 cand = readlane64(ck, src);
+    if (!(cand < b.tk)) continue;                    // the bar moved below it
+    // entries ahead of the candidate; the bar is not, so pos <= k - 1
+    const int pos = __builtin_popcountll(__ballot(b.key < cand));
+    const u64 up = wave_shr1(b.key);
+    b.key = lane > pos ? up : (lane == pos ? cand : b.key);
+    if (lane >= k) b.key = EMPTY;                    // the entry pushed out of the list
+    b.tk = readlane64(b.key, k - 1);
   }
 }
 
@@ -177,7 +228,7 @@ __global__ void __launch_bounds__(64 * QPB) knn_select_encode(const float4* __re
   if (l >= L) return;                                // whole waves leave
   const float4 q = xp[l];
   const float xl = q.x, yl = q.y, zl = q.z;
-  Best b{__builtin_inff(), __builtin_inff(), NO_ATOM, NO_ATOM};
+  Best b{EMPTY, EMPTY};
 
   const int nch = (L + CH - 1) / CH;
   const int c0 = l / CH;
@@ -188,11 +239,11 @@ __global__ void __launch_bounds__(64 * QPB) knn_select_encode(const float4* __re
     const int c = g + lane;
     const bool fresh = c < nch && (c < c0 - 1 || c > c0 + 1);
     const float lb = fresh ? box_bound(xl, yl, zl, box[2 * c], box[2 * c + 1]) : __builtin_inff();
-    uint64_t mask = __ballot(fresh && lb <= b.td);
+    uint64_t mask = __ballot(fresh && lb <= key_d2(b.tk));
     while (mask) {
       const int src = __builtin_ctzll(mask);
       mask &= mask - 1;
-      if (readlane_f(lb, src) > b.td) continue;      // pruned by a later k-th distance
+      if (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(lb), src)) > key_d2(b.tk)) continue;
       scan_chunk(xp, g + src, l, L, k, lane, xl, yl, zl, b);
     }
   }
@@ -200,11 +251,12 @@ __global__ void __launch_bounds__(64 * QPB) knn_select_encode(const float4* __re
   if (lane >= k) return;
   // Every slot is filled when k <= L - 1 and all distances are finite; an
   // empty one (non-finite coordinates) is reported as -1 with the pair of l itself.
-  const bool have = (unsigned)b.bi < (unsigned)L;
-  const int m = have ? b.bi : l;
+  const uint32_t bi = (uint32_t)b.key;
+  const bool have = bi < (uint32_t)L;
+  const int m = have ? (int)bi : l;
   const float4 pm = xp[m];
   const float dx = xl - pm.x, dy = yl - pm.y, dz = zl - pm.z;
-  const float ph[4] = {dx, dy, dz, 1.0f / (1.0f + (have ? b.bd : 0.f))};
+  const float ph[4] = {dx, dy, dz, 1.0f / (1.0f + (have ? key_d2(b.key) : 0.f))};
   const float4* al = reinterpret_cast<const float4*>(ab + (size_t)l * 2 * CP);
   const float4* bm = reinterpret_cast<const float4*>(ab + (size_t)m * 2 * CP + CP);
   float v[CP];
@@ -252,7 +304,7 @@ hipError_t launch_encode(const float* x, const void* s, int L, int k, const void
   float4* xp = reinterpret_cast<float4*>(base + w.xp);
   float4* box = reinterpret_cast<float4*>(base + w.box);
   const int nch = (L + CH - 1) / CH;
-  hipLaunchKernelGGL(knn_project, dim3((unsigned)(((size_t)L * 32 + 255) / 256)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(knn_project, dim3((unsigned)((L + 127) / 128)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(s), static_cast<const uint16_t*>(w_l),
                      static_cast<const uint16_t*>(w_m), ab, L);
   hipError_t e = hipGetLastError();
