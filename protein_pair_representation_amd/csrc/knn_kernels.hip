@@ -141,8 +141,27 @@ __device__ __forceinline__ u64 key_of(float d2, int m) { return ((u64)__float_as
 __device__ __forceinline__ float key_d2(u64 key) { return __uint_as_float((uint32_t)(key >> 32)); }
 
 __device__ __forceinline__ u64 join(uint32_t lo, uint32_t hi) { return ((u64)hi << 32) | lo; }
-__device__ __forceinline__ u64 shfl_xor64(u64 v, int j) {
-  return join((uint32_t)__shfl_xor((int)(uint32_t)v, j), (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), j));
+template <int CTRL> __device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL> __device__ __forceinline__ u64 dpp64(u64 v) {
+  return join(dpp32<CTRL>((uint32_t)v), dpp32<CTRL>((uint32_t)(v >> 32)));
+}
+// The key of lane (lane ^ J): DPP inside a row of 16 lanes (quad permutes for
+// 1 and 2; a rotation right by n gives lane i the value of lane (i - n) mod 16,
+// so lane ^ 4 is a rotation by 4 or 12 and lane ^ 8 one by 8), the LDS
+// crossbar across rows.
+template <int J> __device__ __forceinline__ u64 xor_lane(u64 v, int lane) {
+  if constexpr (J == 1) return dpp64<0xB1>(v);                 // quad_perm [1,0,3,2]
+  else if constexpr (J == 2) return dpp64<0x4E>(v);            // quad_perm [2,3,0,1]
+  else if constexpr (J == 4) {
+    // both rotations run on every lane before the select (a DPP move inside a
+    // branch would read lanes the branch switched off)
+    const u64 down = dpp64<0x124>(v), up = dpp64<0x12C>(v);  // row_ror 4 / 12
+    return (lane & 4) ? down : up;
+  }
+  else if constexpr (J == 8) return dpp64<0x128>(v);           // row_ror 8
+  else return join((uint32_t)__shfl_xor((int)(uint32_t)v, J), (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), J));
 }
 __device__ __forceinline__ u64 shfl64(u64 v, int src) {
   return join((uint32_t)__shfl((int)(uint32_t)v, src), (uint32_t)__shfl((int)(uint32_t)(v >> 32), src));
@@ -156,31 +175,36 @@ __device__ __forceinline__ u64 readlane64(u64 v, int lane) {
               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane));
 }
 
-// Bitonic sort of one key per lane into ascending lane order.
-__device__ __forceinline__ u64 sort64(u64 key, int lane) {
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1)
-#pragma unroll
-    for (int j = size >> 1; j > 0; j >>= 1) {
-      const u64 other = shfl_xor64(key, j);
-      const bool keep_min = ((lane & j) == 0) == ((lane & size) == 0);
-      key = keep_min ? (other < key ? other : key) : (other > key ? other : key);
-    }
+// One compare-exchange step of a bitonic network: the lower lane of each pair
+// keeps the smaller key when `ascending`, the larger otherwise.
+template <int J> __device__ __forceinline__ u64 exchange(u64 key, int lane, bool ascending) {
+  const u64 other = xor_lane<J>(key, lane);
+  const bool keep_min = ((lane & J) == 0) == ascending;
+  return keep_min ? (other < key ? other : key) : (other > key ? other : key);
+}
+
+// Bitonic merge of a bitonic sequence of 2J keys per block into ascending
+// (or descending) order.
+template <int J> __device__ __forceinline__ u64 merge_steps(u64 key, int lane, bool ascending) {
+  key = exchange<J>(key, lane, ascending);
+  if constexpr (J > 1) key = merge_steps<J / 2>(key, lane, ascending);
   return key;
 }
+
+// Bitonic sort of one key per lane into ascending lane order: blocks of
+// SIZE lanes sorted alternately up and down, then merged.
+template <int SIZE> __device__ __forceinline__ u64 sort_steps(u64 key, int lane) {
+  if constexpr (SIZE > 2) key = sort_steps<SIZE / 2>(key, lane);
+  return merge_steps<SIZE / 2>(key, lane, (lane & SIZE) == 0);
+}
+__device__ __forceinline__ u64 sort64(u64 key, int lane) { return sort_steps<64>(key, lane); }
 
 // The 64 smallest of two ascending lists, ascending: the elementwise minimum of
 // one list and the other reversed is a bitonic sequence holding them; a
 // bitonic merge sorts it.
 __device__ __forceinline__ u64 merge64(u64 list, u64 batch, int lane) {
   const u64 rev = shfl64(batch, 63 - lane);
-  u64 key = rev < list ? rev : list;
-#pragma unroll
-  for (int j = 32; j > 0; j >>= 1) {
-    const u64 other = shfl_xor64(key, j);
-    key = (lane & j) == 0 ? (other < key ? other : key) : (other > key ? other : key);
-  }
-  return key;
+  return merge_steps<32>(rev < list ? rev : list, lane, true);
 }
 
 // The best list of one query wave: one key per lane (lanes >= k hold EMPTY);
@@ -198,7 +222,9 @@ __device__ __forceinline__ void scan_chunk(const float4* __restrict__ xp, int c,
   const bool beats = ok && ck < b.tk;
   uint64_t mask = __ballot(beats);
   if (__builtin_popcountll(mask) > NINS) {           // many: sort the chunk, merge it in
-    const u64 merged = merge64(b.key, sort64(beats ? ck : EMPTY, lane), lane);
+    const u64 sorted = sort64(beats ? ck : EMPTY, lane);
+    const u64 merged = readlane64(b.key, 0) == EMPTY ? sorted      // the list is empty
+                                                     : merge64(b.key, sorted, lane);
     b.key = lane < k ? merged : EMPTY;
     b.tk = readlane64(b.key, k - 1);
     return;
