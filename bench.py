@@ -379,6 +379,7 @@ def summarize_trace(run_dir, workload, steps, warmup, family="tri"):
         summ = f"python3 bench.py --summarize-trace $O/kt --workload {workload} --steps {steps} --family aaq"
         sha, path = kernel_sha(AAQ_SRC), os.path.join(PROFILE_DIR, f"aaq_{workload}_trace.txt")
     elif family == "knn":
+        workload = "knn-L16384-k32"
         run = f"python3 $R/bench.py --knn-only --steps {steps}"
         summ = f"python3 bench.py --summarize-trace $O/kt --steps {steps} --family knn"
         sha, path = kernel_sha(KNN_SRC), os.path.join(PROFILE_DIR, "knn_knn-L16384-k32_trace.txt")
