@@ -515,11 +515,10 @@ def main():
         assert torch.isfinite(out[v]).all(), f"non-finite output ({v})"
 
     ms_step = (t1 - t0) * 1e3 / args.steps
-    k1_ms = sum(e[3 * n_].elapsed_time(e[3 * n_ + 1]) for e in events for n_ in range(len(variants)))
-    k2_ms = sum(e[3 * n_ + 1].elapsed_time(e[3 * n_ + 2]) for e in events for n_ in range(len(variants)))
-    n_launch = args.steps * len(variants)
-    k1_ms /= n_launch
-    k2_ms /= n_launch
+    k1_all = sorted(e[3 * n_].elapsed_time(e[3 * n_ + 1]) for e in events for n_ in range(len(variants)))
+    k2_all = sorted(e[3 * n_ + 1].elapsed_time(e[3 * n_ + 2]) for e in events for n_ in range(len(variants)))
+    k1_ms = sum(k1_all) / len(k1_all)
+    k2_ms = sum(k2_all) / len(k2_all)
 
     step_flops = 0.0
     for v in variants:
@@ -546,9 +545,12 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": k2_bytes(I, R, es),
                      "flops_per_launch": k2_flops, "avg_launch_ms": round(k2_ms, 4)},
         "kernels": {"project_stage (tri_project + tri_pack_bias)": {"avg_ms": round(k1_ms, 4), "algorithmic_bytes": k1b,
+                                    "min_ms": round(k1_all[0], 4), "median_ms": round(k1_all[len(k1_all) // 2], 4),
                                     "GB/s": round(k1b / (k1_ms * 1e-3) / 1e9, 1),
                                     "frac_hbm": round(k1b / (k1_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-                    "tri_attend": {"avg_launch_ms": round(k2_ms, 4), "TFLOP/s": round(k2_tflops, 2)}},
+                    "tri_attend": {"avg_launch_ms": round(k2_ms, 4), "TFLOP/s": round(k2_tflops, 2),
+                                   "min_launch_ms": round(k2_all[0], 4),
+                                   "median_launch_ms": round(k2_all[len(k2_all) // 2], 4)}},
         "kernel_sha": kernel_sha(),
     }
     if args.key_blocks > 0 and variants[0] != "rows":
