@@ -302,7 +302,7 @@ def _short(name):
     for key in ("tri_attend", "tri_project", "tri_pack_bias", "copyBuffer"):
         if key in name:
             return key
-    m = re.search(r"aaq_(encode|decode)_([ABC])_(bf16|f32)|knn_(project|boxes|select_encode)", name)
+    m = re.search(r"aaq_(encode|decode)_([ABC])_(bf16|f32)|knn_(prepare|select_encode)", name)
     if m:
         return m.group(0)
     return name[:60]

@@ -11,11 +11,10 @@
 //    N(l), c_s = 128 single channels (bf16), c_p = 16 pair channels, stored bf16.
 //
 // Kernels, in launch order:
-//  * knn_project: A = s W_l^T and B = s W_m^T per atom (fp32, [L][2][16]), the
-//    single-feature halves of every pair, computed once per atom on MFMA;
-//  * knn_boxes: one wave per chunk of 64 consecutive atoms: the coordinates
-//    copied as float4 (one 16-byte load per candidate later) and the chunk's
-//    axis-aligned bounding box;
+//  * knn_prepare: A = s W_l^T and B = s W_m^T per atom (fp32, [L][2][16]), the
+//    single-feature halves of every pair, computed once per atom on MFMA; and,
+//    per chunk of 64 consecutive atoms, the coordinates copied as float4 (one
+//    16-byte load per candidate later) and the chunk's axis-aligned bounding box;
 //  * knn_select_encode: one wave per query atom.  Lanes 0..k-1 hold the best
 //    list found so far, sorted by (d2, index); lane 63 down to k hold +inf.
 //    Chunks are scanned 64 candidates at a time (one per lane).  When many
@@ -62,11 +61,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // and rows 8 (i / 4) + 4 (q >> 5) + (i % 4), i = 0..15.  A = W with its rows
 // permuted so that lane q's 16 results are the consecutive channels
 // 16 (q >> 5) + i of atom (q & 31): one 64-byte store per lane.
-__global__ void __launch_bounds__(256) knn_project(const uint16_t* __restrict__ s, const uint16_t* __restrict__ w_l,
-                                                   const uint16_t* __restrict__ w_m, float* __restrict__ ab, int L) {
-  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
-  const int atom0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 32;
-  if (atom0 >= L) return;
+__device__ __forceinline__ void project_wave(const uint16_t* __restrict__ s, const uint16_t* __restrict__ w_l,
+                                             const uint16_t* __restrict__ w_m, float* __restrict__ ab, int L,
+                                             int atom0, int lane) {
+  const int h = lane >> 5, r = lane & 31;
   const int o = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);     // channel of result row r
   const uint16_t* wrow = o < CP ? w_l + (size_t)o * CS : w_m + (size_t)(o - CP) * CS;
   const int atom = atom0 + r;
@@ -88,9 +86,10 @@ __global__ void __launch_bounds__(256) knn_project(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------- chunk boxes
-__global__ void __launch_bounds__(CH) knn_boxes(const float* __restrict__ x, int L, float4* __restrict__ xp,
-                                                float4* __restrict__ box) {
-  const int c = blockIdx.x, lane = threadIdx.x;
+// One wave per chunk c of 64 atoms: the coordinates as float4 (padding atoms
+// past L hold 0 and are never candidates) and the chunk's bounding box.
+__device__ __forceinline__ void box_wave(const float* __restrict__ x, int L, float4* __restrict__ xp,
+                                         float4* __restrict__ box, int c, int lane) {
   const int m = c * CH + lane;
   const bool ok = m < L;
   const float px = ok ? x[3 * (size_t)m] : 0.f, py = ok ? x[3 * (size_t)m + 1] : 0.f,
@@ -112,6 +111,20 @@ __global__ void __launch_bounds__(CH) knn_boxes(const float* __restrict__ x, int
     box[2 * c] = make_float4(lx, ly, lz, 0.f);
     box[2 * c + 1] = make_float4(hx, hy, hz, 0.f);
   }
+}
+
+// Both preparation passes in one launch: workgroup b covers atoms
+// [128 b, 128 b + 128): wave w projects atoms 128 b + 32 w .. + 31, and waves 0
+// and 1 also build chunks 2 b and 2 b + 1.
+__global__ void __launch_bounds__(256) knn_prepare(const uint16_t* __restrict__ s, const uint16_t* __restrict__ w_l,
+                                                   const uint16_t* __restrict__ w_m, float* __restrict__ ab,
+                                                   const float* __restrict__ x, int L, float4* __restrict__ xp,
+                                                   float4* __restrict__ box) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = 2 * blockIdx.x + wave;
+  if (wave < 2 && c < (L + CH - 1) / CH) box_wave(x, L, xp, box, c, lane);
+  const int atom0 = (4 * blockIdx.x + wave) * 32;
+  if (atom0 < L) project_wave(s, w_l, w_m, ab, L, atom0, lane);
 }
 
 // ---------------------------------------------------------------- selection + pairs
@@ -329,14 +342,10 @@ hipError_t launch_encode(const float* x, const void* s, int L, int k, const void
   float* ab = reinterpret_cast<float*>(base + w.ab);
   float4* xp = reinterpret_cast<float4*>(base + w.xp);
   float4* box = reinterpret_cast<float4*>(base + w.box);
-  const int nch = (L + CH - 1) / CH;
-  hipLaunchKernelGGL(knn_project, dim3((unsigned)((L + 127) / 128)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(knn_prepare, dim3((unsigned)((L + 127) / 128)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(s), static_cast<const uint16_t*>(w_l),
-                     static_cast<const uint16_t*>(w_m), ab, L);
+                     static_cast<const uint16_t*>(w_m), ab, x, L, xp, box);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(knn_boxes, dim3((unsigned)nch), dim3(CH), 0, stream, x, L, xp, box);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(knn_select_encode, dim3((unsigned)((L + QPB - 1) / QPB)), dim3(64 * QPB), 0, stream, xp, box,
                      ab, w_d, L, k, nbr, static_cast<uint16_t*>(pair));
