@@ -174,3 +174,17 @@ def test_workload_16384():
     assert np.array_equal(nbr[rows], idx)
     check_pairs(a, pair[rows], want, idx, rows, "sampled rows")
     ranks_are_exact(a["x"].numpy(), nbr.astype(np.int64), k)
+
+
+@pytest.mark.parametrize("L,k", [(100003, 64), (1 << 20, 32)])
+def test_large_sampled(L, k):
+    """Large and ragged atom counts (past the 16384-atom workload): sampled rows
+    against the oracle, every sampled list bit-exact."""
+    say(f"[knn] large L={L} k={k}")
+    a = inputs.make_atoms(40 + k, L)
+    nbr, pair = run(a, k)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.r_[0:8, L - 8:L, rng.integers(0, L, 48)])
+    idx, want = oracle(a, k, rows)
+    assert np.array_equal(nbr[rows], idx)
+    check_pairs(a, pair[rows], want, idx, rows, f"L={L} sampled rows")
