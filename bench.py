@@ -230,7 +230,14 @@ def cpu_baseline(wl, z_host, w_host, target_s=20.0):
     proj, attn, out = flops(I, done, False)
     total_f = f_bias + proj + attn + out
     total_t = t_bias + t_rows
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(total_f / total_t / 1e12, 5), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"{wl.name}: the whole pair bias ({workers} BLAS threads) + starting-node rows {done} of {I} "
                       f"({workers} processes, 1 BLAS thread each), float64 NumPy; {total_t:.1f} s wall"}
 
