@@ -130,3 +130,28 @@ def test_zero_tokens_is_a_no_op():
     y = aaq.aaq_decode(rec, "A", torch.bfloat16)
     torch.cuda.synchronize()
     assert rec.shape == (0, 160) and y.shape == (0, 128)
+
+
+@pytest.mark.parametrize("group", ["A", "B"])
+def test_large_count(group):
+    """2^25 + 3 tokens (8.6 GB of bf16, element offsets past 2^32) drawn on the
+    device with 1% of the values scaled by 20: sampled records, at both ends and
+    across the 2^31-byte and 2^32-element marks, byte for byte against the
+    oracle's encoding, and their decodes bit for bit."""
+    n = (1 << 25) + 3
+    say(f"[aaq] large count n={n} group {group}")
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    x = torch.randn((n, 128), generator=gen, device="cuda")
+    spikes = torch.rand((n, 128), generator=gen, device="cuda") < 0.01
+    x = torch.where(spikes, x * 20.0, x).to(torch.bfloat16)
+    del spikes
+    rec = aaq.aaq_encode(x, group)
+    y = aaq.aaq_decode(rec, group, torch.bfloat16)
+    torch.cuda.synchronize()
+    rb = aaq.aaq_record_bytes(group)
+    marks = [0, (1 << 31) // 256, (1 << 31) // rb, (1 << 32) // 128, n - 64]
+    idx = np.unique(np.concatenate([np.arange(m, min(m + 64, n)) for m in marks]))
+    it = torch.as_tensor(idx, device="cuda")
+    x32 = tokens_f32(x[it])
+    want = compare_records(rec[it], x32, group, f"n={n} sampled")
+    assert same_bits(y[it], oracle_decoded(want, group, "bf16"))
