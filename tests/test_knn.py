@@ -188,3 +188,31 @@ def test_large_sampled(L, k):
     idx, want = oracle(a, k, rows)
     assert np.array_equal(nbr[rows], idx)
     check_pairs(a, pair[rows], want, idx, rows, f"L={L} sampled rows")
+
+
+def test_max_atoms():
+    """The largest supported count, 2^24 atoms (k = 32): neighbour lists of
+    sampled rows bit for bit against the oracle's ranking, and their pair
+    features from the oracle's phi and the stored single features."""
+    L, k = 1 << 24, 32
+    say(f"[knn] max atoms L={L} k={k}")
+    a = inputs.make_atoms(77, L)
+    d = {n: t.cuda() for n, t in a.items()}
+    nbr, pair = kn.knn_pair_encode(d["x"], d["s"], k, d["w_l"], d["w_m"], d["w_d"])
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, L // 2, L - 2, L - 1, 12345678, 9876543, 4242424])
+    rt = torch.as_tensor(rows, device="cuda")
+    got_nbr = nbr[rt].cpu().numpy()
+    got_pair = pair[rt].cpu().float().numpy()
+    del d, nbr, pair
+    torch.cuda.empty_cache()
+    x = a["x"].numpy()
+    idx, d2 = oknn.neighbours(x, k, rows)
+    assert np.array_equal(got_nbr, idx)
+    s = inputs.to_f64(a["s"][torch.as_tensor(np.concatenate([rows, idx.ravel()]))])
+    sr, sm = s[:len(rows)], s[len(rows):].reshape(len(rows), k, -1)
+    want = (sr @ inputs.to_f64(a["w_l"]).T)[:, None, :] + sm @ inputs.to_f64(a["w_m"]).T \
+        + oknn.phi(x, rows, idx, d2) @ inputs.to_f64(a["w_d"]).T
+    err = np.abs(got_pair - want)
+    say(f"  L={L}: pair max abs {err.max():.3e}, rel L1 {err.sum() / np.abs(want).sum():.3e}")
+    assert err.sum() / np.abs(want).sum() <= 5e-3 and np.all(err <= 2.0 ** -8 * np.abs(want) + 1e-3)
