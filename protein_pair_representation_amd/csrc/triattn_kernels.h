@@ -36,6 +36,7 @@ struct AttendArgs {
   void* out;
   int I, P, lines;
   int nqb;                // query blocks (set by launch_attend from the block width)
+  int xcd_mode;           // workgroup placement over the XCDs (set by launch_attend)
   int out_transposed;     // 1: out[j][line], 0: out[line][j]
   // key range: tiles kt0 .. kt0+nbt-1 of 64 keys (the whole row: 0, ceil(I/64))
   int kt0, nbt;
