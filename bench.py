@@ -306,7 +306,11 @@ def _per_dispatch(path, counter):
 
 
 def _short(name):
-    for key in ("tri_attend", "tri_project", "tri_pack_bias", "copyBuffer"):
+    if "tri_attend" in name:
+        # the unshifted form (template flag true) does the work of one-pass calls;
+        # the shifted form only runs the workgroups it flags (or key-block calls)
+        return "tri_attend" if ("Lb1E" in name or "true>" in name) else "tri_attend_shifted"
+    for key in ("tri_project", "tri_pack_bias", "copyBuffer"):
         if key in name:
             return key
     m = re.search(r"aaq_(encode|decode)_([ABC])_(bf16|f32)|knn_(prepare|select_encode)", name)

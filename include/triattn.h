@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TRIATTN_ABI_VERSION 3
+#define TRIATTN_ABI_VERSION 4
 
 /* Compute dtypes. */
 enum { TA_BF16 = 1, TA_F32 = 2 };
@@ -121,12 +121,16 @@ typedef struct ta_weights {
  *   bias_f32 fp32 [H][I][I]  start/end only: the pair bias as K1 computes it,
  *                            bias_f32[h][line][pos] = b^h of token (line, pos),
  *                            natural-log units (absent, (size_t)-1, for rows)
+ *   redo int32 [ceil(L/2) * ceil(I/128)]  one flag per attention workgroup
+ *                            (2 lines x 128 queries): set when one of its heads
+ *                            needs a softmax shift, so that only these
+ *                            workgroups run the shifted form of the kernel
  * For the end variant line = column j of Z and position = row i.
  * The attention kernel works in base 2 on shifted logits: exp2(q.k + bias - m)
  * is the softmax numerator exp(q.k/sqrt(d) + b) up to a factor common to the
  * query's row, which the normalisation removes.                              */
 typedef struct ta_ws_layout {
-  size_t q, k, vt, g, o, bias, bias_f32; /* byte offsets */
+  size_t q, k, vt, g, o, bias, bias_f32, redo; /* byte offsets */
   size_t total;             /* bytes required */
   int32_t lines, positions; /* L and padded P */
 } ta_ws_layout;

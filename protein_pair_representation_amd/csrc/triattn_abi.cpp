@@ -57,13 +57,17 @@ void layout_of(const ta_problem* p, int variant, ta_ws_layout* l) {
   // every variant: the packed bias the attention kernel reads (tiled)
   l->bias = 5 * region;
   const size_t packed = align256((size_t)kHeads * P * P * esize(p->dtype));
+  size_t end;
   if (variant == TA_ROWS) {  // the caller supplies the fp32 bias
     l->bias_f32 = (size_t)-1;
-    l->total = l->bias + packed;
+    end = l->bias + packed;
   } else {                   // K1 writes the fp32 bias here, then it is packed
     l->bias_f32 = l->bias + packed;
-    l->total = l->bias_f32 + align256((size_t)kHeads * p->I * p->I * sizeof(float));
+    end = l->bias_f32 + align256((size_t)kHeads * p->I * p->I * sizeof(float));
   }
+  // per-workgroup flags of the attention kernel's unshifted form
+  l->redo = end;
+  l->total = end + align256(triattn::attend_redo_flags((int)lines, p->I) * sizeof(int32_t));
 }
 
 int check_weights(const ta_weights* w) {
@@ -148,6 +152,7 @@ triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weigh
   a.out_transposed = variant == TA_END ? 1 : 0;
   a.kt0 = 0;
   a.nbt = (p->I + kKeyTile - 1) / kKeyTile;  // every key
+  a.redo = (int*)(base + l.redo);            // used by one-pass calls only
   return a;
 }
 

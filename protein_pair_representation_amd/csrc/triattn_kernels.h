@@ -45,10 +45,15 @@ struct AttendArgs {
   float* state_ml;
   int state_in;           // 1: start every head from the state instead of empty
   int state_out;          // 1: store the state at the end of every head (no gate, no output projection)
+  // one-pass calls: one flag per workgroup (attend_redo_flags), written by the
+  // unshifted form, read by the shifted form; nullptr: the shifted form only
+  int* redo;
 };
 
 hipError_t launch_project(const ProjectArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& a, int dtype, hipStream_t stream);
+// number of int32 flags launch_attend needs in AttendArgs::redo for `lines` lines of I keys
+size_t attend_redo_flags(int lines, int I);
 // tiled dst(h, j, k) = max((src[h][j][k] - max_k src[h][j][k]) * log2(e), -30000) in the
 // compute dtype; keys >= I -30000, query rows >= I zero
 hipError_t launch_pack_bias(const float* src, void* dst, int I, int P, int dtype, hipStream_t stream);

@@ -598,6 +598,35 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], typename El<T>::
   return l0 + l1;
 }
 
+// The same exponentials for the unshifted form of the key loop: the row sum is
+// accumulated into la / lb across tiles instead of being returned per tile.
+template <typename T>
+__device__ __forceinline__ void exp_tile_acc(const f32x16 (&s)[2], typename El<T>::frag (&pf)[2][2], float& la,
+                                             float& lb) {
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float p[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) p[t] = fast_exp2(s[st][8 * c + t]);
+      pf[st][c] = to_frag<T>(p);
+      if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          bf16x2 pr = {pf[st][c][2 * t], pf[st][c][2 * t + 1]};
+          if (t & 1) lb = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lb, false);
+          else la = __builtin_amdgcn_fdot2_f32_bf16(pr, one, la, false);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) { la += p[t]; lb += p[t + 1]; }
+      }
+    }
+}
+
 // Rare path: move the shift m up to the tile's exact maximum, rescale O and l,
 // shift the scores and re-exponentiate.  Returns the tile sum; d = the amount
 // m moved (scores computed earlier with the old m must be shifted by it too).
@@ -699,7 +728,16 @@ __device__ __forceinline__ void out_projection(const AttendArgs& a, int line0, i
 
 // ROWS consecutive lines per workgroup (each wave works on all of them for its
 // 32 queries, so one bias tile serves ROWS rows), WAVES waves = 32*WAVES queries.
-template <typename T, int ROWS, int WAVES, int MIN_WAVES_PER_SIMD>
+//
+// Two forms.  UNSHIFTED (one-pass calls): every head runs with m = 0 and no test
+// inside a key tile; a workgroup that meets a head needing a shift (its first key
+// tile's maximum outside [-64, 64], or a row sum past 2^64) sets its flag in
+// a.redo and stores nothing more.  The shifted form (lazy m as described above)
+// then runs only the flagged workgroups of the same grid when a.redo is given,
+// and every workgroup otherwise (key-block calls).  The two forms are separate
+// kernels so that the unshifted one is compiled on its own, with the registers
+// for three waves per SIMD.
+template <typename T, int ROWS, int WAVES, int MIN_WAVES_PER_SIMD, bool UNSHIFTED>
 __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(AttendArgs a) {
   typedef typename El<T>::frag frag;
   typedef typename El<T>::bias_t BT;
@@ -716,7 +754,11 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
   constexpr int EPU = 16 / El<T>::bytes;           // elements per 16-B unit
   constexpr int QBW = 32 * WAVES;                  // queries per workgroup
   __shared__ u32x4 kv_lds[2][STAGE_UNITS];         // [buffer][row][K tile | V^T tile]
+  __shared__ int redo_flag;                        // UNSHIFTED: some wave needs the shifted form
 
+  if constexpr (!UNSHIFTED) {
+    if (a.redo != nullptr && a.redo[blockIdx.x] == 0) return;   // done by the unshifted form
+  }
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, lr = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar addressing
   const int I = a.I, P = a.P;
@@ -803,6 +845,8 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
     kt = g - h * nbt;
   };
   bfrag bias_next[4];
+  if (tid == 0) redo_flag = 0;
+  bool bad = false;                                // UNSHIFTED: this lane saw a head that needs a shift
   if (nbt > 0) {
     load_tile(0, kt0);
     store_tile(0);
@@ -826,7 +870,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       mact[r] = false;
       lsum[r] = 0.f;
       o[r] = zero;
-      if (a.state_in) {
+      if (!UNSHIFTED && a.state_in) {
         // carried state: shift m, sum l (held by the lower half) and unnormalised O
         const size_t sq = ((size_t)line_of(r) * NH + h) * P + j;
         const float2 ml = *reinterpret_cast<const float2*>(a.state_ml + 2 * sq);
@@ -921,10 +965,92 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       __syncthreads();
     };
 
-    if (nbt > 0) tile(0, std::true_type{});
-    for (int kt = 1; kt < nbt; ++kt) tile(kt, std::false_type{});
+    // The unshifted form of a key tile: the same products and exponentials with
+    // m = 0 and no test inside the tile, so the scheduler can interleave one row's
+    // products with the other row's exponentials.  It leaves the conditions under
+    // which the shifted form would have introduced a shift in `bad` (the first
+    // tile's maximum outside [-64, 64], or a row sum past 2^64 -- a tile sum past
+    // it makes the running sum pass it too, as every term is >= 0; NaN counts).
+    auto tile_unshifted = [&](int kt, auto first_tag, float (&la)[ROWS], float (&lb)[ROWS]) {
+      constexpr bool FIRST = decltype(first_tag)::value;
+      const int g = h * nbt + kt, buf = g & 1;
+      int hn, ktn;
+      split(g + 1, hn, ktn);
+      load_tile(hn, kt0 + ktn);
+      f32x16 sbias[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) sbias[st] = mma(esel[0], bias_next[2 * st], zero);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) sbias[st] = mma(esel[1], bias_next[2 * st + 1], sbias[st]);
+      load_bias(bias0 + hn * bias_head + ((size_t)(kt0 + ktn) << 11), bias_next);
+      f32x16 sc[ROWS][2];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const u32x4* kl = kv_lds[buf] + r * ROW_UNITS;
+        frag kf[2][2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) kf[st][c] = lds_frag<T, KU>(kl, 32 * st + rho(lr), 2 * c + hh);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) sc[r][st] = mma(kf[st][0], qf[r][0], sbias[st]);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) sc[r][st] = mma(kf[st][1], qf[r][1], sc[r][st]);
+      }
+      if constexpr (FIRST) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          const float mx = tile_max(sc[r]);
+          bad = bad || mx > FIRST_LIMIT || mx < -FIRST_LIMIT;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const u32x4* vl = kv_lds[buf] + r * ROW_UNITS + KTILE_UNITS;
+        frag pf[2][2];
+        exp_tile_acc<T>(sc[r], pf, la[r], lb[r]);
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            frag vf = lds_frag<T, VU>(vl, rho(lr), 4 * st + 2 * hh + c);
+            o[r] = mma(vf, pf[st][c], o[r]);
+          }
+      }
+      if constexpr (sizeof(T) == 2 && ROWS == 2) {
+        // issue order: the bias and row-0 score products, then each of row 1's
+        // score products and row 0's P.V products beside 16 VALU instructions
+        // (the exponentials, conversions and sums of the other row), then row
+        // 1's P.V products
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+      store_tile(buf ^ 1);
+      __syncthreads();
+    };
 
-    if (a.state_out) {
+    if constexpr (UNSHIFTED) {
+      float la[ROWS], lb[ROWS];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) la[r] = lb[r] = 0.f;
+      tile_unshifted(0, std::true_type{}, la, lb);
+      for (int kt = 1; kt < nbt; ++kt) tile_unshifted(kt, std::false_type{}, la, lb);
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        lsum[r] = la[r] + lb[r];
+        bad = bad || !(lsum[r] <= SUM_LIMIT);
+      }
+    } else {
+      if (nbt > 0) tile(0, std::true_type{});
+      for (int kt = 1; kt < nbt; ++kt) tile(kt, std::false_type{});
+    }
+
+    if (!UNSHIFTED && a.state_out) {
       // ---- key-block mode: carry (m, l, O) to the next block
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
@@ -954,6 +1080,14 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
     }
   }
 
+  if constexpr (UNSHIFTED) {
+    // the workgroup's verdict: any lane of any wave that needs a shift
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo_flag = 1;
+    __syncthreads();
+    const bool redo = redo_flag != 0;
+    if (tid == 0) a.redo[blockIdx.x] = redo ? 1 : 0;
+    if (redo) return;                              // the shifted form redoes this workgroup
+  }
   static_assert(2 * STAGE_UNITS >= CZ * CZ * El<T>::bytes / 16, "W_o must fit in the K/V staging area");
   if (!a.state_out) out_projection<T, ROWS, NT>(a, line0, j, hh, lr, &kv_lds[0][0]);
 }
@@ -1048,11 +1182,19 @@ hipError_t launch_pack_bias(const float* src, void* dst, int I, int P, int dtype
 #define TRIATTN_ROWS 2
 #endif
 #ifndef TRIATTN_MINW
-#define TRIATTN_MINW 2  // waves per SIMD the bf16 attention kernel is compiled for
+#define TRIATTN_MINW 2  // waves per SIMD the bf16 attention kernel (shifted form) is compiled for
+#endif
+#ifndef TRIATTN_MINW_UNSHIFTED
+#define TRIATTN_MINW_UNSHIFTED 3  // and its unshifted form
 #endif
 #ifndef TRIATTN_WAVES
 #define TRIATTN_WAVES 4
 #endif
+
+size_t attend_redo_flags(int lines, int I) {
+  constexpr int R = TRIATTN_ROWS, W = TRIATTN_WAVES;
+  return (size_t)((lines + R - 1) / R) * (size_t)((I + 32 * W - 1) / (32 * W));
+}
 
 hipError_t launch_attend(const AttendArgs& args, int dtype, hipStream_t stream) {
   constexpr int R = TRIATTN_ROWS, W = TRIATTN_WAVES;
@@ -1060,11 +1202,18 @@ hipError_t launch_attend(const AttendArgs& args, int dtype, hipStream_t stream) 
   a.nqb = (a.I + 32 * W - 1) / (32 * W);
   a.xcd_mode = a.I < 2048 ? 2 : 0;
   const long nblk = (long)((a.lines + R - 1) / R) * a.nqb;
-  // bf16: two waves per SIMD; fp32 (twice the fragment registers): one
-  if (dtype == 1)
-    hipLaunchKernelGGL((tri_attend<__bf16, R, W, TRIATTN_MINW>), dim3((unsigned)nblk), dim3(W * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((tri_attend<float, R, W, 1>), dim3((unsigned)nblk), dim3(W * 64), 0, stream, a);
+  const bool one_pass = !a.state_in && !a.state_out && a.redo != nullptr && a.nbt > 0;
+  if (!one_pass) a.redo = nullptr;
+  const dim3 g((unsigned)nblk), b(W * 64);
+  // bf16: the unshifted form at three waves per SIMD, the shifted form at two;
+  // fp32 (twice the fragment registers): one
+  if (dtype == 1) {
+    if (one_pass) hipLaunchKernelGGL((tri_attend<__bf16, R, W, TRIATTN_MINW_UNSHIFTED, true>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((tri_attend<__bf16, R, W, TRIATTN_MINW, false>), g, b, 0, stream, a);
+  } else {
+    if (one_pass) hipLaunchKernelGGL((tri_attend<float, R, W, 1, true>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((tri_attend<float, R, W, 1, false>), g, b, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ class TaWeights(ctypes.Structure):
 class TaWsLayout(ctypes.Structure):
     _fields_ = [("q", ctypes.c_size_t), ("k", ctypes.c_size_t), ("vt", ctypes.c_size_t),
                 ("g", ctypes.c_size_t), ("o", ctypes.c_size_t), ("bias", ctypes.c_size_t),
-                ("bias_f32", ctypes.c_size_t),
+                ("bias_f32", ctypes.c_size_t), ("redo", ctypes.c_size_t),
                 ("total", ctypes.c_size_t),
                 ("lines", ctypes.c_int32), ("positions", ctypes.c_int32)]
 

@@ -46,7 +46,7 @@ def test_exports_match_header(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.triangle_attn_abi_version() == 3
+    assert lib.triangle_attn_abi_version() == 4
     for code in range(0, -12, -1):
         msg = lib.triangle_attn_strerror(code).decode()
         assert msg and msg != "unknown error code"
@@ -90,10 +90,12 @@ def test_layout_sizes(lib, I, rows, variant, dtype):
     assert lay.bias == 5 * region
     packed = (4 * P * P * es + 255) // 256 * 256
     if variant == ta.TA_ROWS:
-        assert lay.bias_f32 == ctypes.c_size_t(-1).value and lay.total == 5 * region + packed
+        assert lay.bias_f32 == ctypes.c_size_t(-1).value and lay.redo == 5 * region + packed
     else:
         assert lay.bias_f32 == 5 * region + packed
-        assert lay.total == lay.bias_f32 + (4 * I * I * 4 + 255) // 256 * 256
+        assert lay.redo == lay.bias_f32 + (4 * I * I * 4 + 255) // 256 * 256
+    # one int32 flag per attention workgroup of 2 lines x 128 queries
+    assert lay.total == lay.redo + (((lines + 1) // 2) * ((I + 127) // 128) * 4 + 255) // 256 * 256
 
 
 def _start(lib, p=None, w="default", z=A, out=A + 100 * MB, ws=A + 200 * MB, ws_bytes=1 << 40, fn="start"):

@@ -162,6 +162,76 @@ def test_repeatable_bitwise():
     assert torch.equal(a, b)
 
 
+# ------------------------------------------------------------------ heads that need a softmax shift
+# One-pass attention first runs every head without a shift (scores used as
+# base-2 exponents directly) and runs a head again with the lazily introduced
+# shift when its first key tile lies more than 64 (base 2) from 0 or a row sum
+# passes 2^64.  These cases force that second run.
+
+@pytest.mark.parametrize("I,R,dtype,qsel", [(130, 8, "bf16", None), (257, 5, "bf16", (32, 64)),
+                                             (200, 4, "f32", None), (257, 3, "f32", (200, 232))])
+def test_first_key_tile_far_below(I, R, dtype, qsel):
+    """Keys 0..63 (the first key tile) carry a bias 60 below N(0, 1) for all
+    queries, or for one 32-query block only (then one wave of the workgroup asks
+    for the shifted form and the whole workgroup takes it)."""
+    say(f"[parity] shift: first key tile far below, I={I} R={R} {dtype} queries={qsel}")
+    w = weights_with_extras(400 + I, dtype)
+    zr = inputs.make_z_rows(400 + I, I, 0, R, dtype)
+    bias = inputs.random_bias(400 + I, 4, I)
+    q = slice(None) if qsel is None else slice(*qsel)
+    bias[:, q, :64] -= 60.0
+    out = ta.triangle_attn_start_rows(zr.cuda(), bias.cuda(), dev(w))
+    torch.cuda.synchronize()
+    check(out, ref.triangle_attn_rows(inputs.to_f64(zr), inputs.to_f64(bias), params64(w)), dtype,
+          "first tile far below")
+
+
+def test_shift_flags_do_not_carry_over():
+    """One workspace for three row-block calls: a bias that needs the shifted form
+    in some workgroups, then an ordinary one, then the first again.  Each call
+    sets every workgroup's flag afresh, so each result matches its own oracle."""
+    I, R = 257, 6
+    say(f"[parity] shift flags over reused workspace I={I} R={R}")
+    w = weights_with_extras(450, "bf16")
+    zr = inputs.make_z_rows(450, I, 0, R, "bf16")
+    plain = inputs.random_bias(451, 4, I)
+    far = plain.clone()
+    far[:, 100:180, :64] -= 60.0
+    ws = ta.workspace(I, R, torch.bfloat16, "rows")
+    want = {}
+    for name, b in (("far", far), ("plain", plain), ("far again", far)):
+        out = ta.triangle_attn_start_rows(zr.cuda(), b.cuda(), dev(w), ws=ws)
+        torch.cuda.synchronize()
+        key = "far" if name.startswith("far") else "plain"
+        if key not in want:
+            want[key] = ref.triangle_attn_rows(inputs.to_f64(zr), inputs.to_f64(b), params64(w))
+        check(out, want[key], "bf16", name)
+
+
+def test_large_logits_f32():
+    """W_q and W_k scaled by 6: logits with a standard deviation of ~50 (base 2),
+    so first key tiles reach past 64 and row sums past 2^64 (exp2 itself would
+    overflow fp32 past 128).  The bar is looser than the fp32 one: the scores are
+    accumulated in fp32 from terms up to ~40 in size, so they carry errors up to
+    ~1e-4 (natural-log units); a perturbation ds of the scores moves a softmax
+    average of v by at most 2 max|ds| max|v| (|v| < 8 here), and the output
+    projection does not amplify it beyond 2e-3."""
+    I = 200
+    say(f"[parity] shift: large logits I={I} f32")
+    w = weights_with_extras(500, "f32")
+    w["w_q"] = w["w_q"] * 6.0
+    w["w_k"] = w["w_k"] * 6.0
+    z = inputs.make_z(500, I, "f32")
+    out = ta.triangle_attn_start(z.cuda(), dev(w))
+    torch.cuda.synchronize()
+    got = inputs.to_f64(out)
+    want = ref.triangle_attn_start(inputs.to_f64(z), params64(w))
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - want).max()
+    say(f"    large logits: max abs {err:.3e}")
+    assert err <= 2e-3
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_gate(dtype):
     say(f"[invariant] zero gate {dtype}")
