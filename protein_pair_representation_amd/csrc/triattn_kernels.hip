@@ -1110,7 +1110,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
   }
 
   if constexpr (UNSHIFTED) {
-    // the workgroup's verdict: any lane of any wave that needs a shift
+    // the workgroup's decision: any lane of any wave that needs a shift
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo_flag = 1;
     __syncthreads();
     const bool redo = redo_flag != 0;
