@@ -164,12 +164,14 @@ def test_repeatable_bitwise():
 
 # ------------------------------------------------------------------ heads that need a softmax shift
 # One-pass attention first runs every head without a shift (scores used as
-# base-2 exponents directly) and runs a head again with the lazily introduced
-# shift when its first key tile lies more than 64 (base 2) from 0 or a row sum
-# passes 2^64.  These cases force that second run.
+# base-2 exponents directly); a workgroup (2 lines x 128 queries) runs again with
+# the lazily introduced shift when one of its heads has a first key tile whose
+# maximum lies more than 64 (base 2) from 0, or a row sum past 2^64.  These cases
+# force that second run, for a few workgroups or for the whole grid.
 
 @pytest.mark.parametrize("I,R,dtype,qsel", [(130, 8, "bf16", None), (257, 5, "bf16", (32, 64)),
-                                             (200, 4, "f32", None), (257, 3, "f32", (200, 232))])
+                                             (200, 4, "f32", None), (257, 3, "f32", (200, 232)),
+                                             (1024, 6, "bf16", None), (1024, 6, "bf16", (512, 544))])
 def test_first_key_tile_far_below(I, R, dtype, qsel):
     """Keys 0..63 (the first key tile) carry a bias 60 below N(0, 1) for all
     queries, or for one 32-query block only (then one wave of the workgroup asks
