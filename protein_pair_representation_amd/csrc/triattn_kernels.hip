@@ -865,13 +865,20 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
   const BT* bias0 = (const BT*)a.bias + ((size_t)(jb < jb_last ? jb : jb_last) * (P >> 6) << 11);
   const size_t bias_head = (size_t)P * P;        // elements per head; key tile stride 2048
 
-  // step g = h * nbt + kt walks the key tiles kt0 + kt of every head (past the
-  // end: the last tile again, unused)
-  const int ntiles = NH * nbt;
-  auto split = [&](int g, int& h, int& kt) {
-    g = g < ntiles ? g : ntiles - 1;
-    h = g / nbt;
-    kt = g - h * nbt;
+  // step g = h * nbt + kt walks the key tiles kt0 + kt of every head; the step
+  // after (h, kt) is (h, kt + 1), the next head's first tile, or past the end
+  // the last tile again (loaded, unused)
+  auto next_tile = [&](int h, int kt, int& hn, int& ktn) {
+    hn = h;
+    ktn = kt + 1;
+    if (ktn == nbt) {
+      hn = h + 1;
+      ktn = 0;
+    }
+    if (hn == NH) {
+      hn = NH - 1;
+      ktn = nbt - 1;
+    }
   };
   bfrag bias_next[4];
   if (tid == 0) redo_flag = 0;
@@ -924,7 +931,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       constexpr bool FIRST = decltype(first_tag)::value;
       const int g = h * nbt + kt, buf = g & 1;
       int hn, ktn;
-      split(g + 1, hn, ktn);
+      next_tile(h, kt, hn, ktn);
       load_tile(hn, kt0 + ktn);                             // stage the next tile
       f32x16 sbias[2];
 #pragma unroll
@@ -1004,7 +1011,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       constexpr bool FIRST = decltype(first_tag)::value;
       const int g = h * nbt + kt, buf = g & 1;
       int hn, ktn;
-      split(g + 1, hn, ktn);
+      next_tile(h, kt, hn, ktn);
       load_tile(hn, kt0 + ktn);
       f32x16 sbias[2];
 #pragma unroll
