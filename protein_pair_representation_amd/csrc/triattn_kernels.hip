@@ -1142,18 +1142,51 @@ __global__ void __launch_bounds__(NTHREADS) tri_pack_bias(const float* __restric
   for (int r = blockIdx.x; r < NH * rows_pad; r += gridDim.x) {
     const int h = r / rows_pad, j = r % rows_pad;
     const float* s = src + ((size_t)h * I + j) * I;
+    // four consecutive keys per thread: one 16-B read when the row is 16-B aligned,
+    // and one contiguous run of the tiled layout to write
+    const bool vec = (reinterpret_cast<uintptr_t>(s) & 15) == 0;
+    auto load4 = [&](int k0, float (&v)[4]) {
+      if (vec && k0 + 3 < I) {
+        const float4 f = *reinterpret_cast<const float4*>(s + k0);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = k0 + t < I ? s[k0 + t] : -INFINITY;
+      }
+    };
     float mx = -INFINITY;
     if (j < I)
-      for (int k = threadIdx.x; k < I; k += NTHREADS) mx = fmaxf(mx, s[k]);
+      for (int c = threadIdx.x; c < ((I + 3) >> 2); c += NTHREADS) {
+        float v[4];
+        load4(c << 2, v);
+        mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+      }
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
     __syncthreads();
     mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();  // red is reused by the next row
-    for (int k = threadIdx.x; k < P; k += NTHREADS) {
-      float v = k < I ? (j < I ? (s[k] - mx) * LOG2E : 0.f) : MASKED;
-      v = v < MASKED ? MASKED : v;  // NaN stays NaN
-      dst[bias_tiled_index(h, j, k, P)] = (BT)v;
+    for (int c = threadIdx.x; c < (P >> 2); c += NTHREADS) {
+      const int k0 = c << 2;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (j < I) load4(k0, v);
+      BT out4[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float x = k0 + t < I ? (j < I ? (v[t] - mx) * LOG2E : 0.f) : MASKED;
+        x = x < MASKED ? MASKED : x;  // NaN stays NaN
+        out4[t] = (BT)x;
+      }
+      BT* d = dst + bias_tiled_index(h, j, k0, P);
+      if constexpr (sizeof(BT) == 2) {
+        uint2 w;
+        __builtin_memcpy(&w, out4, 8);
+        *reinterpret_cast<uint2*>(d) = w;
+      } else {
+        u32x4 w;
+        __builtin_memcpy(&w, out4, 16);
+        *reinterpret_cast<u32x4*>(d) = w;
+      }
     }
   }
 }
