@@ -191,7 +191,9 @@ int triangle_attn_project(const ta_problem* prob, int variant, const ta_weights*
  * is required for TA_ROWS (natural-log units, [H][I][I]; it is first packed,
  * shifted per query and scaled by log2(e), into the workspace) and must be NULL
  * otherwise (the workspace already holds it).  Writes the workspace's `o`
- * region (and, for TA_ROWS, its packed bias). */
+ * and `redo` regions (and, for TA_ROWS, its packed bias).  Enqueues two
+ * kernels: the attention without a softmax shift, then the shifted form for the
+ * workgroups the first one flagged (the others return at once). */
 int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* w,
                          const float* bias, void* out, void* ws, size_t ws_bytes,
                          void* stream);
