@@ -761,7 +761,8 @@ __device__ __forceinline__ void out_projection(const AttendArgs& a, int line0, i
 // Two forms.  UNSHIFTED (one-pass calls): every head runs with m = 0 and no test
 // inside a key tile; a workgroup that meets a head needing a shift (its first key
 // tile's maximum outside [-64, 64], or a row sum past 2^64) sets its flag in
-// a.redo and stores nothing more.  The shifted form (lazy m as described above)
+// a.redo at the end and skips the output projection (the shifted form rewrites
+// its gated head outputs in o).  The shifted form (lazy m as described above)
 // then runs only the flagged workgroups of the same grid when a.redo is given,
 // and every workgroup otherwise (key-block calls).  The two forms are separate
 // kernels so that the unshifted one is compiled on its own, with the registers
