@@ -188,28 +188,64 @@ __device__ __forceinline__ void encode_body(const T* __restrict__ x, int64_t n, 
     float s_o = 0.0f;
     int nout = 0;
     if (F::OUTL) {
-      // Section 2.2.2.  Mean and population deviation of the token (float64, two passes);
-      // flagged: |x - mu| > 3 sigma.
-      double d[VPL];
-      double s1 = 0.0;
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        d[j] = (double)v[j];
-        s1 += d[j];
-      }
-      s1 = octet(s1, [](double a, double b) { return a + b; });
-      const double mu = s1 / 128.0;
-      double s2 = 0.0;
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        d[j] = d[j] - mu;
-        s2 = __builtin_fma(d[j], d[j], s2);
-      }
-      s2 = octet(s2, [](double a, double b) { return a + b; });
-      const double lim = 3.0 * __builtin_sqrt(s2 / 128.0);
+      // Section 2.2.2.  Mean and population deviation of the token (two passes);
+      // flagged: |x - mu| > 3 sigma.  The flags are those of float64 arithmetic.
+      // They are first taken in float32; a wave whose tokens hold a value within
+      // 2^-12 (max|x| + 3 sigma) of its limit takes them again in float64.  The
+      // float32 pass is off by far less: each sum has at most 19 roundings over 128
+      // terms of size <= max|x|, so mu is within 2e-6 max|x|, each |x - mu| within
+      // 3e-6 max|x| and the limit within 3e-5 of itself.
       uint32_t fl = 0;  // bit j: value j is flagged (built from the top bit down: fl = 2 fl + flag)
+      {
+        float s1f = 0.0f, amax = 0.0f;
 #pragma unroll
-      for (int j = VPL - 1; j >= 0; --j) fl = fl + fl + (__builtin_fabs(d[j]) > lim ? 1u : 0u);
+        for (int j = 0; j < VPL; ++j) {
+          s1f += v[j];
+          amax = fmaxf(amax, fabsf(v[j]));
+        }
+        s1f = octet(s1f, [](float a, float b) { return a + b; });
+        amax = octet(amax, [](float a, float b) { return fmaxf(a, b); });
+        const float muf = s1f * (1.0f / 128.0f);
+        float df[VPL];
+        float s2f = 0.0f;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          df[j] = v[j] - muf;
+          s2f = __builtin_fmaf(df[j], df[j], s2f);
+        }
+        s2f = octet(s2f, [](float a, float b) { return a + b; });
+        const float limf = 3.0f * __builtin_sqrtf(s2f * (1.0f / 128.0f));
+        const float margin = 0x1p-12f * (amax + limf);
+        bool near = !(margin < __builtin_inff());   // inf / NaN: float64 decides
+#pragma unroll
+        for (int j = VPL - 1; j >= 0; --j) {
+          const float a = fabsf(df[j]);
+          fl = fl + fl + (a > limf ? 1u : 0u);
+          near = near || fabsf(a - limf) <= margin;
+        }
+        if (__ballot(near) != 0) {
+          double d[VPL];
+          double s1 = 0.0;
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            d[j] = (double)v[j];
+            s1 += d[j];
+          }
+          s1 = octet(s1, [](double a, double b) { return a + b; });
+          const double mu = s1 / 128.0;
+          double s2 = 0.0;
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            d[j] = d[j] - mu;
+            s2 = __builtin_fma(d[j], d[j], s2);
+          }
+          s2 = octet(s2, [](double a, double b) { return a + b; });
+          const double lim = 3.0 * __builtin_sqrt(s2 / 128.0);
+          fl = 0;
+#pragma unroll
+          for (int j = VPL - 1; j >= 0; --j) fl = fl + fl + (__builtin_fabs(d[j]) > lim ? 1u : 0u);
+        }
+      }
 
       uint32_t outm = 0;  // bit j: value j of this lane is a confirmed outlier
       if (__ballot(fl != 0) != 0) {
