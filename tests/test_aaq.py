@@ -1,7 +1,8 @@
 """GPU parity of the AAQ codec (aaq_encode / aaq_decode through the C ABI).
 
 The bar is bit-exactness: both sides take every code-making decision in
-float32 with the same operations, and the 3-sigma test in float64.  The only
+float32 with the same operations, and the 3-sigma test as float64 decides it
+(the kernel takes it in float32 and again in float64 near the limit).  The only
 allowed difference is a token whose float64 3-sigma test lies within 1e-9
 (relative) of its threshold, where the two summation orders may decide
 differently; such tokens are counted and left out of the byte comparison, and
@@ -69,6 +70,44 @@ def test_encode_decode_mixed(group, dtype, n):
         want_rec = compare_records(rec, x32, group, f"encode {group} {dtype} n={n}")
         assert same_bits(y, oracle_decoded(want_rec, group, out_dt)), f"decode {group} -> {out_dt}"
     assert bool(torch.all(buf[:4096] == 0xA5)) and bool(torch.all(buf[-4096:] == 0xA5)), "write outside records"
+
+
+def spike_at_limit(y: np.ndarray) -> float:
+    """The value x > mean(y) for which |x - mu| = 3 sigma over the token [y, x]
+    (float64 bisection)."""
+    def excess(x):
+        t = np.append(y, x)
+        return abs(x - t.mean()) - 3.0 * t.std()
+    lo, hi = float(y.mean()), float(y.mean()) + 100.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        lo, hi = (mid, hi) if excess(mid) < 0 else (lo, mid)
+    return 0.5 * (lo + hi)
+
+
+@pytest.mark.parametrize("group", ["A", "B"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_three_sigma_boundary(group, dtype):
+    """Tokens whose spike sits 1e-7 .. 1e-3 (relative) below or above its token's
+    3-sigma limit.  Within about 2.4e-4 of the limit the kernel takes the flags
+    again in float64, farther out it keeps its float32 ones; every record must
+    equal the oracle's either way.  (bf16 rounding of the spike moves it by up to
+    2^-9, so bf16 tokens land at random distances around the limit.)"""
+    say(f"[aaq] 3-sigma boundary {dtype} group {group}")
+    rng = np.random.default_rng(31)
+    offs = [sg * m for m in (1e-7, 1e-6, 1e-5, 3e-5, 1e-4, 2e-4, 3e-4, 1e-3) for sg in (-1.0, 1.0)]
+    rows = []
+    for i in range(48):
+        y = rng.standard_normal(127)
+        y = torch.from_numpy(y).to(TDT[dtype]).to(torch.float64).numpy()
+        x = spike_at_limit(y)
+        for o in offs:
+            rows.append(np.insert(y, i % 128, x * (1.0 + o)))
+    x = torch.from_numpy(np.array(rows)).to(TDT[dtype])
+    x32 = tokens_f32(x)
+    rec = aaq.aaq_encode(x.cuda(), group)
+    torch.cuda.synchronize()
+    compare_records(rec, x32, group, f"3-sigma boundary {group} {dtype}")
 
 
 @pytest.mark.parametrize("group", ["A", "B", "C"])
