@@ -203,7 +203,10 @@ def cpu_baseline(wl, z_host, w_host, target_s=20.0):
     from oracle import ref
     from protein_pair_representation_amd import inputs
 
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    # one process per core of this process's CPU share, at most 16: the share of one GPU
+    # on the GPU hosts (a box may show more cores than it allots to one GPU)
+    allowed = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, allowed))
     I = wl.I
     p = ref.params(inputs.weights_f64(w_host), 4, 32)
     z64 = inputs.to_f64(z_host)
@@ -237,7 +240,8 @@ def cpu_baseline(wl, z_host, w_host, target_s=20.0):
     except OSError:
         pass
     return {"value": round(total_f / total_t / 1e12, 5), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
-            "cpu_model": cpu_model,
+            "cpu_model": cpu_model, "host_cpu_count": os.cpu_count(), "cores_in_affinity": allowed,
+            "cores_note": "workers = cores of this process's affinity, capped at 16 (one GPU's CPU share)",
             "sample": f"{wl.name}: the whole pair bias ({workers} BLAS threads) + starting-node rows {done} of {I} "
                       f"({workers} processes, 1 BLAS thread each), float64 NumPy; {total_t:.1f} s wall"}
 
@@ -307,9 +311,12 @@ def _per_dispatch(path, counter):
 
 def _short(name):
     if "tri_attend" in name:
-        # the unshifted form (template flag true) does the work of one-pass calls;
-        # the shifted form only runs the workgroups it flags (or key-block calls)
-        return "tri_attend" if ("Lb1E" in name or "true>" in name) else "tri_attend_shifted"
+        # the one-pass kernels (bf16: tri_attend_fast; fp32: the unshifted form, template
+        # flag true) do the work of one-pass calls; the shifted form only runs the
+        # workgroups they flag (or key-block calls)
+        if "tri_attend_fast" in name or "Lb1E" in name or "true>" in name:
+            return "tri_attend"
+        return "tri_attend_shifted"
     for key in ("tri_project", "tri_pack_bias", "copyBuffer"):
         if key in name:
             return key
@@ -357,7 +364,7 @@ def summarize_pmc(run_dir, workload, copy_mib, family="tri"):
     else:
         wl_path = os.path.join(PROFILE_DIR, f"tri_attend_{workload}_pmc.txt")
         sha = kernel_sha()
-        cmd_b = f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline --key-blocks 0 --aaq 0 --knn 0"
+        cmd_b = f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline --key-blocks 0 --aaq 0 --knn 0 --other-workloads 0"
         tail = [f"traffic_bytes_per_launch={per.get('tri_attend', 0.0):.6e} kernel_sha={sha}",
                 f"tri_project_traffic_bytes_per_launch={per.get('tri_project', 0.0):.6e} kernel_sha={sha}"]
     cmd_c = f"python3 $R/bench.py --copy-calibration {copy_mib}"
@@ -375,6 +382,88 @@ def summarize_pmc(run_dir, workload, copy_mib, family="tri"):
            *tail]
     open(wl_path, "w").write("\n".join(txt) + "\n")
     print("\n".join(txt))
+
+
+SQ_PASSES = [
+    "GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES "
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_VALU2 SQ_WAIT_INST_ANY SQ_WAIT_ANY",
+    "GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS "
+    "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_ANY",
+    "GRBM_GUI_ACTIVE SQ_INSTS_VMEM SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_SCA SQ_WAVES SQ_BUSY_CU_CYCLES",
+]
+
+
+def summarize_sq(run_dir, workload):
+    """Write the attention kernel's SQ counter summary (matrix-core and VALU activity).
+
+    run_dir holds sq1/ sq2/ sq3/: bench.py under the three counter sets of SQ_PASSES.
+    rocprofv3 reports each counter summed over the device; GRBM_GUI_ACTIVE is summed
+    over the 8 XCDs, so one XCD's busy cycles are GRBM_GUI_ACTIVE / 8, and the
+    fractions below are per SIMD: counter / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs),
+    with the quad-cycle counters (SQ_ACTIVE_INST_*) multiplied by 4.
+    """
+    import collections
+    import csv
+    import glob
+    acc = collections.defaultdict(list)
+    durations = []
+    for n in range(1, len(SQ_PASSES) + 1):
+        files = glob.glob(os.path.join(run_dir, f"sq{n}", "**", "*counter_collection.csv"), recursive=True)
+        if len(files) != 1:
+            raise SystemExit(f"expected one counter_collection.csv under {run_dir}/sq{n}")
+        per = collections.defaultdict(dict)
+        for r in csv.DictReader(open(files[0])):
+            if _short(r["Kernel_Name"]) != "tri_attend":
+                continue
+            per[r["Dispatch_Id"]][r["Counter_Name"]] = float(r["Counter_Value"])
+            if n == 1 and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                durations.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+        for d in per.values():
+            for k, v in d.items():
+                acc[k].append(v)
+    c = {k: sum(v) / len(v) for k, v in acc.items()}
+    xcd_cycles = c["GRBM_GUI_ACTIVE"] / 8
+    simd_cycles = xcd_cycles * 1024
+    dur = sum(durations) / len(durations)
+    waves = c.get("SQ_WAVES", 0.0)
+
+    def frac(name, quad=False):
+        return c[name] * (4 if quad else 1) / simd_cycles
+
+    mfma, valu, coex = frac("SQ_VALU_MFMA_BUSY_CYCLES"), frac("SQ_ACTIVE_INST_VALU", True), \
+        frac("SQ_VALU_MFMA_COEXEC_CYCLES")
+    lines = [f"# SQ counters of the one-pass attention kernel (tri_attend), workload {workload}, gfx950 (MI355X)",
+             "# commands (R = repository root, O = output directory, run from /tmp), n = 1, 2, 3 over the counter sets:"]
+    for n, pset in enumerate(SQ_PASSES, 1):
+        lines.append(f"#   timeout -s KILL 100 rocprofv3 --pmc {pset} --output-format csv -d $O/sq{n} -o s -- "
+                     f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline "
+                     "--key-blocks 0 --aaq 0 --knn 0 --other-workloads 0")
+    lines.append(f"#   python3 bench.py --summarize-sq $O --workload {workload}")
+    lines.append(f"# kernel_sha={kernel_sha()}")
+    lines.append("# normalisation: per SIMD, counter / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs);"
+                 " SQ_ACTIVE_INST_* are in quad-cycles (x 4)")
+    lines += [f"{k:28s} {v:18.1f}" for k, v in sorted(c.items())]
+    lines += [
+        f"dispatches_per_pass        {len(durations)}",
+        f"avg_dispatch_ms            {dur * 1e3:.4f}",
+        f"effective_clock_ghz        {xcd_cycles / dur / 1e9:.3f}   (GRBM_GUI_ACTIVE / 8 / dispatch time)",
+        f"mfma_busy                  {mfma:.4f}   (SQ_VALU_MFMA_BUSY_CYCLES per SIMD-cycle)",
+        f"valu_active                {valu:.4f}   (4 x SQ_ACTIVE_INST_VALU per SIMD-cycle; MFMA issue included)",
+        f"mfma_valu_coexec           {coex:.4f}   (SQ_VALU_MFMA_COEXEC_CYCLES per SIMD-cycle)",
+        f"mfma_or_valu               {mfma + valu - coex:.4f}",
+        f"wave_wait_inst_any         {c['SQ_WAIT_INST_ANY'] * 4 / c['SQ_WAVE_CYCLES']:.4f}   "
+        "(4 x SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)" if "SQ_WAIT_INST_ANY" in c else "",
+    ]
+    if waves:
+        lines += [f"valu_insts_per_wave        {c['SQ_INSTS_VALU'] / waves:.1f}",
+                  f"mfma_insts_per_wave        {c['SQ_INSTS_MFMA'] / waves:.1f}",
+                  f"trans_f32_insts_per_wave   {c['SQ_INSTS_VALU_TRANS_F32'] / waves:.1f}",
+                  f"lds_insts_per_wave         {c['SQ_INSTS_LDS'] / waves:.1f}",
+                  f"salu_insts_per_wave        {c['SQ_INSTS_SALU'] / waves:.1f}",
+                  f"vmem_insts_per_wave        {c['SQ_INSTS_VMEM'] / waves:.1f}"]
+    path = os.path.join(PROFILE_DIR, f"tri_attend_{workload}_sq.txt")
+    open(path, "w").write("\n".join(x for x in lines if x) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_trace(run_dir, workload, steps, warmup, family="tri"):
@@ -396,7 +485,7 @@ def summarize_trace(run_dir, workload, steps, warmup, family="tri"):
         sha, path = kernel_sha(KNN_SRC), os.path.join(PROFILE_DIR, "knn_knn-L16384-k32_trace.txt")
     else:
         run = (f"python3 $R/bench.py --workload {workload} --steps {steps} --warmup {warmup} --no-cpu-baseline "
-               f"--key-blocks 0 --aaq 0 --knn 0")
+               f"--key-blocks 0 --aaq 0 --knn 0 --other-workloads 0")
         summ = f"python3 bench.py --summarize-trace $O/kt --workload {workload} --steps {steps} --warmup {warmup}"
         sha, path = kernel_sha(), os.path.join(PROFILE_DIR, f"kernels_{workload}_trace.txt")
     out = [f"# rocprofv3 kernel statistics, workload {workload}, gfx950 (MI355X)",
@@ -437,6 +526,11 @@ def main():
     ap.add_argument("--knn", type=int, default=1, help="also time the kNN sparse pair encoder (0: skip)")
     ap.add_argument("--knn-only", action="store_true",
                     help="time only the kNN sparse pair encoder (knn-L16384-k32) over --steps calls")
+    ap.add_argument("--other-workloads", type=int, default=1,
+                    help="also measure the other workloads (fewer steps each; 0: skip)")
+    ap.add_argument("--summarize-sq", metavar="DIR",
+                    help="write the attention kernel's SQ counter summary under profiles/ from rocprofv3 --pmc runs "
+                         "in DIR, and exit")
     ap.add_argument("--family", default="tri", choices=["tri", "aaq", "knn"],
                     help="kernel family of --summarize-pmc / --summarize-trace")
     args = ap.parse_args()
@@ -445,6 +539,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.workload, args.steps, args.warmup, args.family)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -470,12 +567,86 @@ def main():
         return
 
     wl = inputs.WORKLOADS[args.workload]
-    dt = inputs.DTYPES[wl.dtype]
-    es = 2 if wl.dtype == "bf16" else 4
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
+    if args.aaq_only:
+        z = inputs.workload_z(wl).to(dev)
+        print(json.dumps({"workload": wl.name, "aaq": aaq_codec(z, wl.name, stream, reps=args.steps)}), flush=True)
+        return
+
+    m = measure_workload(wl, args.steps, args.warmup, stream)
+    res = {
+        "metric": "pair-attention TFLOP/s (bf16) and % of MFMA peak at I=1024, c_z=128",
+        "value": m["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic (seeded N(0,1) pair tensor and weights, resident in HBM)",
+        "config": {"workload": wl.name, "I": wl.I, "rows": wl.n_rows, "c_z": 128, "heads": 4, "head_dim": 32,
+                   "variants": list(wl.variants)},
+        "pct_of_peak_step": m["pct_of_peak_step"],
+        "roofline": m["roofline"],
+        "kernels": m["kernels"],
+        "kernel_sha": kernel_sha(),
+    }
+    z, wd, ws = m.pop("_z"), m.pop("_wd"), m.pop("_ws")
+    variants = list(wl.variants)
+    if args.key_blocks > 0 and variants[0] != "rows":
+        res["key_blocks"] = key_blocks(ws[variants[0]], wd, wl.I, wl.n_rows, inputs.DTYPES[wl.dtype], variants[0],
+                                       args.key_blocks, stream, m["k2_flops"], m["roofline"]["avg_launch_ms"])
+    if args.aaq > 0:
+        res["aaq"] = aaq_codec(z, wl.name, stream)
+        if wl.dtype == "bf16":
+            res["aaq"]["project_stage"] = aaq_project(z, wd, variants[0], stream)
+    if args.knn > 0:
+        res["knn"] = knn_encoder(stream)
+    del z, wd, ws
+    torch.cuda.empty_cache()
+    if args.other_workloads:
+        # the other workloads of the survey, each measured the same way (fewer steps)
+        others = {}
+        for name in inputs.WORKLOADS:
+            if name == wl.name:
+                continue
+            o = inputs.WORKLOADS[name]
+            steps = 10 if o.I < 4096 else 5
+            mo = measure_workload(o, steps, 3, stream)
+            for k in ("_z", "_wd", "_ws"):
+                mo.pop(k)
+            others[name] = {"steps": steps, "warmup": 3, "ms_per_step": mo["ms_per_step"], "TFLOP/s": mo["value"],
+                            "dtype": o.dtype, "roofline": mo["roofline"], "kernels": mo["kernels"]}
+            torch.cuda.empty_cache()
+        res["other_workloads"] = others
+    res["gpu_clock"] = gpu_clock()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, inputs.workload_z(wl), inputs.workload_weights(wl))
+    print(json.dumps(res), flush=True)
+
+
+def gpu_clock():
+    """Shader clock of GPU 0 as rocm-smi reports it right after the timed runs (a snapshot)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(out.stdout)
+        card = data.get("card0") or next(iter(data.values()))
+        sclk = next((v for k, v in card.items() if k.lower().startswith("sclk")), None)
+        mhz = float(re.search(r"([0-9.]+)\s*Mhz", str(sclk), re.I).group(1)) if sclk else None
+        return {"sclk_mhz": mhz, "source": "rocm-smi --showclocks (after the timed region)"}
+    except Exception as e:  # the clock is context; its absence does not fail the bench
+        return {"sclk_mhz": None, "source": f"rocm-smi unavailable: {type(e).__name__}"}
+
+
+def measure_workload(wl, steps, warmup, stream):
+    """Time `steps` steps of a workload (every variant: K1 + bias pack, then K2) with inputs
+    resident in HBM; K1 and K2 are also timed per launch with HIP events on `stream`."""
+    import torch
+    from protein_pair_representation_amd import inputs
+    from protein_pair_representation_amd import triattn as ta
+
+    dt = inputs.DTYPES[wl.dtype]
+    es = 2 if wl.dtype == "bf16" else 4
+    dev = torch.device("cuda:0")
     w_host = inputs.workload_weights(wl)
     wd = {k: v.to(dev) for k, v in w_host.items()}
     I, R = wl.I, wl.n_rows
@@ -489,15 +660,11 @@ def main():
             if r0 < R:
                 parts.append(zb[:R - r0])
         z = torch.cat(parts)[:R].contiguous()
-        z_host = None
+        del parts
     else:
-        z_host = inputs.workload_z(wl)
-        z = z_host.to(dev)
+        z = inputs.workload_z(wl).to(dev)
         bias = None
     torch.cuda.synchronize()
-    if args.aaq_only:
-        print(json.dumps({"workload": wl.name, "aaq": aaq_codec(z, wl.name, stream, reps=args.steps)}), flush=True)
-        return
 
     ws = {v: ta.workspace(I, R, dt, v, dev) for v in variants}
     out = {v: torch.empty((R, I, 128), dtype=dt, device=dev) for v in variants}
@@ -512,25 +679,24 @@ def main():
                                     out=out[v], stream=stream)
             evs[3 * n_ + 2].record(stream)
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     warm = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step(warm)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
+    for s_ in range(steps):
+        step(events[s_])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for v in variants:
-        assert torch.isfinite(out[v]).all(), f"non-finite output ({v})"
+        assert torch.isfinite(out[v]).all(), f"non-finite output ({wl.name} {v})"
 
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_step = (t1 - t0) * 1e3 / steps
     k1_all = sorted(e[3 * n_].elapsed_time(e[3 * n_ + 1]) for e in events for n_ in range(len(variants)))
     k2_all = sorted(e[3 * n_ + 1].elapsed_time(e[3 * n_ + 2]) for e in events for n_ in range(len(variants)))
     k1_ms = sum(k1_all) / len(k1_all)
     k2_ms = sum(k2_all) / len(k2_all)
-
     step_flops = 0.0
     for v in variants:
         proj, attn, o = flops(I, R, v != "rows")
@@ -539,43 +705,25 @@ def main():
     k2_flops = attn1 + out1
     k2_tflops = k2_flops / (k2_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = read_traffic(wl.name)
     k1b = k1_bytes(I, R, es, "rows" not in variants)
     value = step_flops / (ms_step * 1e-3) / 1e12
-
-    res = {
-        "metric": "pair-attention TFLOP/s (bf16) and % of MFMA peak at I=1024, c_z=128",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": wl.dtype, "data": "synthetic (seeded N(0,1) pair tensor and weights, resident in HBM)",
-        "config": {"workload": wl.name, "I": I, "rows": R, "c_z": 128, "heads": 4, "head_dim": 32,
-                   "variants": variants},
-        "pct_of_peak_step": round(100 * value / peak, 2),
+    return {
+        "value": round(value, 2), "ms_per_step": round(ms_step, 4), "pct_of_peak_step": round(100 * value / peak, 2),
+        "k2_flops": k2_flops,
         "roofline": {"kernel": "tri_attend", "bound": "mfma", "achieved": round(k2_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(k2_tflops / peak, 4),
-                     "traffic": traffic, "algorithmic_bytes": k2_bytes(I, R, es),
+                     "traffic": read_traffic(wl.name), "algorithmic_bytes": k2_bytes(I, R, es),
                      "flops_per_launch": k2_flops, "avg_launch_ms": round(k2_ms, 4)},
-        "kernels": {"project_stage (tri_project + tri_pack_bias)": {"avg_ms": round(k1_ms, 4), "algorithmic_bytes": k1b,
-                                    "min_ms": round(k1_all[0], 4), "median_ms": round(k1_all[len(k1_all) // 2], 4),
-                                    "GB/s": round(k1b / (k1_ms * 1e-3) / 1e9, 1),
-                                    "frac_hbm": round(k1b / (k1_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "kernels": {"project_stage (tri_project + tri_pack_bias)": {
+                        "avg_ms": round(k1_ms, 4), "algorithmic_bytes": k1b,
+                        "min_ms": round(k1_all[0], 4), "median_ms": round(k1_all[len(k1_all) // 2], 4),
+                        "GB/s": round(k1b / (k1_ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(k1b / (k1_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
                     "tri_attend": {"avg_launch_ms": round(k2_ms, 4), "TFLOP/s": round(k2_tflops, 2),
                                    "min_launch_ms": round(k2_all[0], 4),
                                    "median_launch_ms": round(k2_all[len(k2_all) // 2], 4)}},
-        "kernel_sha": kernel_sha(),
+        "_z": z, "_wd": wd, "_ws": ws,
     }
-    if args.key_blocks > 0 and variants[0] != "rows":
-        res["key_blocks"] = key_blocks(ws[variants[0]], wd, I, R, dt, variants[0], args.key_blocks, stream,
-                                       k2_flops, k2_ms)
-    if args.aaq > 0:
-        res["aaq"] = aaq_codec(z, wl.name, stream)
-        if wl.dtype == "bf16":
-            res["aaq"]["project_stage"] = aaq_project(z, wd, variants[0], stream)
-    if args.knn > 0:
-        res["knn"] = knn_encoder(stream)
-    if not args.no_cpu_baseline and z_host is not None:
-        res["cpu_baseline"] = cpu_baseline(wl, z_host, w_host)
-    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

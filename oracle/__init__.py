@@ -12,7 +12,8 @@ does, and this package imports nothing from the library.
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``,
 ``tests/test_oracle_aaq.py`` and ``tests/test_oracle_knn.py``
-(brute force, torch CPU library routines, closed forms, invariants, and a
-hand-derived golden case under ``tests/golden/``).  No function is
-"parity unpinned".
+(brute force, torch CPU library routines, closed forms, invariants, and
+hand-derived cases written into those tests: the two-key closed form at
+c_z = 2 in test_oracle.py and the worked INT8 / INT4 records in
+test_oracle_aaq.py).  No function is "parity unpinned".
 """

@@ -124,16 +124,18 @@ def triangle_attn_start(z, p, rows=None):
     return np.stack(out)
 
 
-def triangle_attn_end(z, p, cols=None):
+def triangle_attn_end(z, p, cols=None, bias=None):
     """Ending-node triangle attention, written directly (no transposition of Z).
 
     For every column j: queries q_ij and gates g_ij over i, keys/values k_kj,
     v_kj over k, and bias b_ki: bias_T[h][i][k] = bias[h][k][i].
     ``cols`` (optional) restricts the output to those columns j; the result is
-    then [I][len(cols)][c_z] (all rows i, the chosen columns).
+    then [I][len(cols)][c_z] (all rows i, the chosen columns).  ``bias``
+    (optional) is pair_bias(z, p) computed beforehand, for callers that
+    evaluate the columns in several parts.
     """
     I = z.shape[0]
-    bias = pair_bias(z, p)
+    bias = pair_bias(z, p) if bias is None else bias
     bias_t = np.transpose(bias, (0, 2, 1))
     cols = list(range(I)) if cols is None else list(cols)
     out = np.empty((I, len(cols), z.shape[2]))

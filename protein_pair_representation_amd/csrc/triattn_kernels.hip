@@ -1129,6 +1129,310 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
   if (!a.state_out) out_projection<T, ROWS, NT>(a, line0, j, hh, lr, &kv_lds[0][0]);
 }
 
+// ================================================================ K2: bf16 one-pass form
+// The bf16 unshifted form, rebuilt for the issue rates of gfx950: v_exp_f32 issues
+// about once per 9 cycles per SIMD and overlaps poorly with the matrix core, plain
+// VALU work overlaps it fully, and a wave waits for a load only where it uses it.
+// So, per key tile of 64 keys and two rows:
+//  * the next tile's bias and K/V loads are issued at the top of the tile and
+//    consumed at its end (the compiler may not sink them: a scheduling fence);
+//  * row sums come from the matrix core (v_mfma_f32_16x16x32_bf16 with a 0/1
+//    operand, below) instead of 32 dot products on the VALU;
+//  * the tile runs as four chunks of 32 keys x 32 queries (row r, half st): the
+//    scores of chunk c+1 and the P.V and row-sum products of chunk c-1 go to the
+//    matrix core while the VALU exponentiates chunk c;
+//  * the bias products of the next tile (selector MFMAs) run in the tile's last
+//    phase, once the current tile's scores no longer need their registers.
+// Semantics, workgroup grid, redo flags and epilogue are those of tri_attend's
+// unshifted form.
+
+// Row sums on the matrix core.  v_mfma_f32_16x16x32_bf16 takes, in lane l, row
+// (l & 15) of A and column (l & 15) of B over contraction slots 8*(l >> 4) + t,
+// and returns, in lane l, column (l & 15), rows 4*(l >> 4) + i (i = 0..3).  A P
+// fragment (lane l: query l & 31, eight keys) fed as B puts query n in column n
+// for slot groups 0 and 2 and query n + 16 for groups 1 and 3.  With A = 1 where
+// the slot group's parity equals the row half (row >= 8), row m < 8 of column n
+// sums the fragment's 16 keys of query n and row m >= 8 those of query n + 16.
+__device__ __forceinline__ bf16x8 rowsum_selector(int lane) {
+  const __bf16 v = (((lane >> 4) & 1) == ((lane >> 3) & 1)) ? (__bf16)1.0f : (__bf16)0.0f;
+  return bf16x8{v, v, v, v, v, v, v, v};
+}
+// Lane whose row-sum registers hold the sums of query q (0..31): q < 16 in lanes
+// 0..31 (column q), q >= 16 in lanes 32..63 (column q - 16).
+__device__ __forceinline__ int rowsum_lane(int q) { return q < 16 ? q : q + 16; }
+
+__device__ __forceinline__ f32x4 mma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+#define TA_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+#define TA_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+template <int MIN_WAVES_PER_SIMD>
+__global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(AttendArgs a) {
+  typedef __bf16 T;
+  typedef bf16x8 frag;
+  typedef _Float16 BT;
+  typedef f16x8 bfrag;
+  constexpr int ROWS = 2, WAVES = 4, NT = WAVES * 64;
+  constexpr int KU = HD * 2 / 16;                 // 16-B units per K-tile row (32 channels)
+  constexpr int VU = KT * 2 / 16;                 // 16-B units per V^T-tile row (64 keys)
+  constexpr int KTILE_UNITS = KT * KU;
+  constexpr int VTILE_UNITS = HD * VU;
+  constexpr int ROW_UNITS = KTILE_UNITS + VTILE_UNITS;
+  constexpr int STAGE_UNITS = ROWS * ROW_UNITS;
+  constexpr int LDT = STAGE_UNITS / NT;           // 16-B units staged per thread per tile
+  constexpr int EPU = 8;                          // bf16 elements per 16-B unit
+  constexpr int QBW = 32 * WAVES;                 // queries per workgroup
+  static_assert(STAGE_UNITS % NT == 0 && KTILE_UNITS % NT == 0 && VTILE_UNITS % NT == 0, "staging split");
+  __shared__ u32x4 kv_lds[2][STAGE_UNITS];
+  __shared__ int redo_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, lr = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int I = a.I, P = a.P;
+  const int n_lg = (a.lines + ROWS - 1) / ROWS;
+  int lg, qb;
+  map_block(a.xcd_mode, blockIdx.x, n_lg, a.nqb, lg, qb);
+  const int line0 = lg * ROWS;
+  const int j = qb * QBW + wave * 32 + lr;        // this lane's query
+  const int kt0 = a.kt0, nbt = a.nbt;
+  auto line_of = [&](int r) { return line0 + r < a.lines ? line0 + r : a.lines - 1; };
+  const size_t tok_line = (size_t)NH * P * HD;
+
+  // K/V staging: as in tri_attend (each slot a scalar base plus a per-lane offset)
+  constexpr int SPR = ROW_UNITS / NT;
+  constexpr int SPK = KTILE_UNITS / NT;
+  uint32_t g_off[LDT];
+  int l_off[LDT];
+#pragma unroll
+  for (int s = 0; s < LDT; ++s) {
+    const int r = s / SPR, w = (s % SPR) * NT + tid;
+    if ((s % SPR) < SPK) {
+      const int row = w / KU, u = w % KU;
+      g_off[s] = (uint32_t)(row * HD + u * EPU) * sizeof(T);
+      l_off[s] = r * ROW_UNITS + row * KU + (u ^ swz<KU>(row));
+    } else {
+      const int ww = w - KTILE_UNITS, e = ww / VU, u = ww % VU;
+      g_off[s] = (uint32_t)(e * P + u * EPU) * sizeof(T);
+      l_off[s] = r * ROW_UNITS + KTILE_UNITS + e * VU + (u ^ swz<VU>(e));
+    }
+  }
+  u32x4 sreg[LDT];
+  auto load_tile = [&](int h, int kt) {
+#pragma unroll
+    for (int s = 0; s < LDT; ++s) {
+      const int r = s / SPR;
+      const bool is_k = (s % SPR) < SPK;
+      const T* base = is_k ? (const T*)a.k + line_of(r) * tok_line + ((size_t)h * P + kt * KT) * HD
+                           : (const T*)a.vt + line_of(r) * tok_line + (size_t)h * HD * P + kt * KT;
+      sreg[s] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + g_off[s]);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int s = 0; s < LDT; ++s) kv_lds[buf][l_off[s]] = sreg[s];
+  };
+  auto load_bias = [&](const BT* btile, bfrag (&b)[4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) b[g] = *reinterpret_cast<const bfrag*>(btile + g * 512 + lane * 8);
+  };
+  bfrag esel[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const int t = rho(lr) - 16 * g - 8 * hh;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (u == t) ? 1.0f : 0.0f;
+    esel[g] = to_vec8<bfrag>(v);
+  }
+  const frag rsel = rowsum_selector(lane);
+  const int rs_src = rowsum_lane(lr);
+  const f32x16 zero = {};
+  auto bias_scores = [&](const bfrag (&b)[4], f32x16 (&sb)[2]) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) sb[st] = mma(esel[0], b[2 * st], zero);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) sb[st] = mma(esel[1], b[2 * st + 1], sb[st]);
+  };
+
+  const int jb = qb * WAVES + wave, jb_last = (I - 1) >> 5;
+  const BT* bias0 = (const BT*)a.bias + ((size_t)(jb < jb_last ? jb : jb_last) * (P >> 6) << 11);
+  const size_t bias_head = (size_t)P * P;
+  auto next_tile = [&](int h, int kt, int& hn, int& ktn) {
+    hn = h;
+    ktn = kt + 1;
+    if (ktn == nbt) {
+      hn = h + 1;
+      ktn = 0;
+    }
+    if (hn == NH) {
+      hn = NH - 1;
+      ktn = nbt - 1;
+    }
+  };
+  if (tid == 0) redo_flag = 0;
+  bool bad = false;
+  f32x16 sbias[2];
+  {
+    bfrag b0[4];
+    load_bias(bias0 + ((size_t)kt0 << 11), b0);
+    load_tile(0, kt0);
+    store_tile(0);
+    bias_scores(b0, sbias);
+    __syncthreads();
+  }
+
+#pragma unroll 1
+  for (int h = 0; h < NH; ++h) {
+    frag qf[ROWS][2];
+    f32x16 o[ROWS];
+    f32x4 lacc[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const T* qrow = (const T*)a.q + line_of(r) * tok_line + ((size_t)h * P + j) * HD + 8 * hh;
+      qf[r][0] = gld8<T>(qrow);
+      qf[r][1] = gld8<T>(qrow + 16);
+      o[r] = zero;
+      lacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    auto tile = [&](int kt, auto first_tag) {
+      constexpr bool FIRST = decltype(first_tag)::value;
+      const int g = h * nbt + kt, buf = g & 1;
+      int hn, ktn;
+      next_tile(h, kt, hn, ktn);
+      // the next tile's bias and K/V: issued here, used in the last two phases
+      bfrag bias_nx[4];
+      load_bias(bias0 + hn * bias_head + ((size_t)(kt0 + ktn) << 11), bias_nx);
+      load_tile(hn, kt0 + ktn);
+      TA_FENCE();
+      const u32x4* lds = kv_lds[buf];
+      auto kfr = [&](int c, frag (&kf)[2]) {
+        const u32x4* kl = lds + (c >> 1) * ROW_UNITS;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) kf[cc] = lds_frag<T, KU>(kl, 32 * (c & 1) + rho(lr), 2 * cc + hh);
+      };
+      auto vfr = [&](int c, frag (&vf)[2]) {
+        const u32x4* vl = lds + (c >> 1) * ROW_UNITS + KTILE_UNITS;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) vf[cc] = lds_frag<T, VU>(vl, rho(lr), 4 * (c & 1) + 2 * hh + cc);
+      };
+      auto score = [&](int c, const frag (&kf)[2]) {
+        const int r = c >> 1;
+        f32x16 s = mma(kf[0], qf[r][0], sbias[c & 1]);
+        return mma(kf[1], qf[r][1], s);
+      };
+      float mxr[ROWS] = {-INFINITY, -INFINITY};
+      auto expo = [&](int c, const f32x16& s, frag (&pf)[2]) {
+        if constexpr (FIRST) {
+          float mx = s[0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+          mxr[c >> 1] = fmaxf(mxr[c >> 1], mx);
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          float p[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) p[t] = fast_exp2(s[8 * cc + t]);
+          pf[cc] = to_frag<T>(p);
+        }
+      };
+      auto pv = [&](int c, const frag (&vf)[2], const frag (&pf)[2]) {
+        const int r = c >> 1;
+        o[r] = mma(vf[0], pf[0], o[r]);
+        lacc[r] = mma16(rsel, pf[0], lacc[r]);
+        o[r] = mma(vf[1], pf[1], o[r]);
+        lacc[r] = mma16(rsel, pf[1], lacc[r]);
+      };
+      frag kf0[2], kf1[2], kf2[2], kf3[2], vf0[2], vf1[2], vf2[2], vf3[2];
+      frag pf0[2], pf1[2], pf2[2], pf3[2];
+      // phase 0: scores of chunk 0
+      kfr(0, kf0);
+      kfr(1, kf1);
+      const f32x16 s0 = score(0, kf0);
+      TA_FENCE();
+      // phase 1: scores of chunk 1 | exponentials of chunk 0
+      kfr(2, kf2);
+      vfr(0, vf0);
+      const f32x16 s1 = score(1, kf1);
+      expo(0, s0, pf0);
+      TA_SGB(0x100, 4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 12); }
+      TA_FENCE();
+      // phase 2: scores of chunk 2, P.V of chunk 0 | exponentials of chunk 1
+      kfr(3, kf3);
+      vfr(1, vf1);
+      const f32x16 s2 = score(2, kf2);
+      pv(0, vf0, pf0);
+      expo(1, s1, pf1);
+      TA_SGB(0x100, 4);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 4); }
+      TA_FENCE();
+      // phase 3: scores of chunk 3, P.V of chunk 1 | exponentials of chunk 2
+      vfr(2, vf2);
+      const f32x16 s3 = score(3, kf3);
+      pv(1, vf1, pf1);
+      expo(2, s2, pf2);
+      TA_SGB(0x100, 2);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 4); }
+      TA_FENCE();
+      // phase 4: P.V of chunk 2, the next tile's bias products | exponentials of chunk 3
+      vfr(3, vf3);
+      pv(2, vf2, pf2);
+      bias_scores(bias_nx, sbias);
+      expo(3, s3, pf3);
+      TA_SGB(0x100, 2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 3); }
+      TA_FENCE();
+      // phase 5: P.V of chunk 3; the next tile's K/V into the other buffer
+      pv(3, vf3, pf3);
+      if constexpr (FIRST) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          const float mx = xhalf_max(mxr[r]);
+          bad = bad || mx > FIRST_LIMIT || mx < -FIRST_LIMIT;
+        }
+      }
+      store_tile(buf ^ 1);
+      __syncthreads();
+    };
+
+    if (nbt > 0) tile(0, std::true_type{});
+    for (int kt = 1; kt < nbt; ++kt) tile(kt, std::false_type{});
+
+    // ---- finish head h: row sums, 1/l, gate; o^T (e = 16*hh + i) to the workspace
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const float lsum = __shfl(lacc[r][0], rs_src);
+      bad = bad || !(lsum <= SUM_LIMIT);
+      const float inv = 1.0f / lsum;
+      const size_t tok = line_of(r) * tok_line + ((size_t)h * P + j) * HD + 16 * hh;
+      float gv[16];
+      frag_to_f32<T>(gld8<T>((const T*)a.g + tok), gv);
+      frag_to_f32<T>(gld8<T>((const T*)a.g + tok + 8), gv + 8);
+      float ov[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ov[i] = o[r][i] * inv * gv[i];
+      gst8<T>((T*)a.o + tok, to_frag<T>(ov));
+      gst8<T>((T*)a.o + tok + 8, to_frag<T>(ov + 8));
+    }
+  }
+
+  if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo_flag = 1;
+  __syncthreads();
+  const bool redo = redo_flag != 0;
+  if (tid == 0) a.redo[blockIdx.x] = redo ? 1 : 0;
+  if (redo) return;
+  static_assert(2 * STAGE_UNITS >= CZ * CZ * 2 / 16, "W_o must fit in the K/V staging area");
+  out_projection<T, ROWS, NT>(a, line0, j, hh, lr, &kv_lds[0][0]);
+}
+
 // Bias pack: natural-log fp32 bias [H][I][I] (from K1 or the caller) into the
 // attention kernel's tiled layout (fp16 for bf16 problems, fp32 for fp32).  Each query row is
 // shifted by its own maximum before the base-2 scale and the rounding: the
@@ -1260,6 +1564,9 @@ hipError_t launch_pack_bias(const float* src, void* dst, int I, int P, int dtype
 #ifndef TRIATTN_WAVES
 #define TRIATTN_WAVES 4
 #endif
+#ifndef TRIATTN_MINW_FAST
+#define TRIATTN_MINW_FAST 2  // waves per SIMD of the bf16 one-pass kernel
+#endif
 
 size_t attend_redo_flags(int lines, int I) {
   constexpr int R = TRIATTN_ROWS, W = TRIATTN_WAVES;
@@ -1278,7 +1585,7 @@ hipError_t launch_attend(const AttendArgs& args, int dtype, hipStream_t stream) 
   // bf16: the unshifted form at three waves per SIMD, the shifted form at two;
   // fp32 (twice the fragment registers): one
   if (dtype == 1) {
-    if (one_pass) hipLaunchKernelGGL((tri_attend<__bf16, R, W, TRIATTN_MINW_UNSHIFTED, true>), g, b, 0, stream, a);
+    if (one_pass) hipLaunchKernelGGL((tri_attend_fast<TRIATTN_MINW_FAST>), g, b, 0, stream, a);
     hipLaunchKernelGGL((tri_attend<__bf16, R, W, TRIATTN_MINW, false>), g, b, 0, stream, a);
   } else {
     if (one_pass) hipLaunchKernelGGL((tri_attend<float, R, W, 1, true>), g, b, 0, stream, a);

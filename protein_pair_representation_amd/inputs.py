@@ -26,6 +26,8 @@ Recipe (every workload):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -114,7 +116,8 @@ def make_z_rows(seed: int, I: int, row0: int, n_rows: int, dtype: str = "bf16",
     z_blocks = ch[1].spawn(n_blocks_total)
     m_blocks = ch[2].spawn(n_blocks_total)
     out = torch.empty((n_rows, I, c_z), dtype=DTYPES[dtype])
-    for b in range(b0, b1 + 1):
+
+    def block(b):
         r_lo = b * Z_BLOCK_ROWS
         r_hi = min(I, r_lo + Z_BLOCK_ROWS)
         zb = np.random.default_rng(z_blocks[b]).standard_normal(
@@ -129,6 +132,14 @@ def make_z_rows(seed: int, I: int, row0: int, n_rows: int, dtype: str = "bf16",
             zb += (2.0 * np.exp(-np.abs(i - j) / 32.0)).astype(np.float32)[:, :, None]
         s_lo, s_hi = max(r_lo, row0), min(r_hi, row0 + n_rows)
         out[s_lo - row0:s_hi - row0] = torch.from_numpy(zb[s_lo - r_lo:s_hi - r_lo]).to(DTYPES[dtype])
+
+    # blocks are independent (own generators, disjoint rows of out): drawn on threads
+    blocks = range(b0, b1 + 1)
+    if len(blocks) == 1:
+        block(b0)
+    else:
+        with ThreadPoolExecutor(max(1, min(8, len(os.sched_getaffinity(0)), len(blocks)))) as ex:
+            list(ex.map(block, blocks))
     return out
 
 
