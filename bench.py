@@ -274,6 +274,45 @@ def key_blocks(ws, wd, I, R, dt, variant, nb, stream, k2_flops, k2_ms, reps=10):
             "time_vs_one_pass": round(ms / k2_ms, 3)}
 
 
+def kv_blocks(ws, wd, I, R, dt, variant, nb, stream, k2_flops, k2_ms, reps=10):
+    """The ring step: NB caller-held key blocks (copies of the workspace's keys, values and
+    bias columns, padded to 64 positions) folded into a carried state, then finalize."""
+    import torch
+    from protein_pair_representation_amd import triattn as ta
+    v = ta.workspace_views(ws, I, R, dt, variant)
+    size = (I + nb - 1) // nb
+    blocks = []
+    for k0 in range(0, I, size):
+        nk = min(size, I - k0)
+        npos = (nk + 63) // 64 * 64
+        kb = torch.zeros(v["k"].shape[:2] + (npos, 32), dtype=dt, device="cuda")
+        vb = torch.zeros(v["vt"].shape[:3] + (npos,), dtype=dt, device="cuda")
+        kb[:, :, :nk] = v["k"][:, :, k0:k0 + nk]
+        vb[:, :, :, :nk] = v["vt"][:, :, :, k0:k0 + nk]
+        blocks.append((kb, vb, v["bias_f32"][:, :, k0:k0 + nk].contiguous(), nk))
+    st = ta.state(I, R, dt, variant)
+    out = torch.empty((R, I, 128), dtype=dt, device="cuda")
+
+    def once():
+        for n, (kb, vb, bb, nk) in enumerate(blocks):
+            ta.triangle_attn_attend_kv_block(ws, wd, I, R, dt, kb, vb, bb, nk, n == 0, st, variant=variant,
+                                             stream=stream)
+        ta.triangle_attn_attend_finalize(ws, wd, I, R, dt, st, variant=variant, out=out, stream=stream)
+
+    once()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        once()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"variant": variant, "blocks": len(blocks), "block_keys": size, "ms": round(ms, 4),
+            "TFLOP/s": round(k2_flops / (ms * 1e-3) / 1e12, 2), "one_pass_ms": round(k2_ms, 4),
+            "time_vs_one_pass": round(ms / k2_ms, 3)}
+
+
 def _limit_blas():
     from threadpoolctl import threadpool_limits
     threadpool_limits(limits=1)
@@ -592,8 +631,13 @@ def main():
     z, wd, ws = m.pop("_z"), m.pop("_wd"), m.pop("_ws")
     variants = list(wl.variants)
     if args.key_blocks > 0 and variants[0] != "rows":
-        res["key_blocks"] = key_blocks(ws[variants[0]], wd, wl.I, wl.n_rows, inputs.DTYPES[wl.dtype], variants[0],
-                                       args.key_blocks, stream, m["k2_flops"], m["roofline"]["avg_launch_ms"])
+        dt = inputs.DTYPES[wl.dtype]
+        v0, k2ms = variants[0], m["roofline"]["avg_launch_ms"]
+        res["key_blocks"] = key_blocks(ws[v0], wd, wl.I, wl.n_rows, dt, v0, args.key_blocks, stream,
+                                       m["k2_flops"], k2ms)
+        # caller-held blocks (the ring step): as many blocks, then half as many larger ones
+        res["kv_blocks"] = [kv_blocks(ws[v0], wd, wl.I, wl.n_rows, dt, v0, nb, stream, m["k2_flops"], k2ms)
+                            for nb in sorted({args.key_blocks, max(1, args.key_blocks // 2)}, reverse=True)]
     if args.aaq > 0:
         res["aaq"] = aaq_codec(z, wl.name, stream)
         if wl.dtype == "bf16":

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TRIATTN_ABI_VERSION 4
+#define TRIATTN_ABI_VERSION 5
 
 /* Compute dtypes. */
 enum { TA_BF16 = 1, TA_F32 = 2 };
@@ -221,6 +221,42 @@ int triangle_attn_state_bytes(const ta_problem* prob, int variant, size_t* bytes
 int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_weights* w,
                                const float* bias, int32_t key0, int32_t nkeys, int32_t first,
                                float* state, void* ws, size_t ws_bytes, void* stream);
+
+/* Key-block stage on a block the caller holds: the ring step of that sharding.
+ * The device keeps its queries (q and the gate, in `ws`, from
+ * triangle_attn_project) and receives one block of keys and values at a time,
+ * e.g. the k and v^T regions another device's triangle_attn_project wrote for
+ * its key positions, together with the bias of this device's queries against
+ * those keys.  One call folds the block into the carried state exactly as
+ * triangle_attn_attend_block does for a key range of the workspace; blocks may
+ * come in any order, and once every key has been folded exactly once
+ * triangle_attn_attend_finalize gives what triangle_attn_attend gives (up to
+ * rounding).  To fold several blocks in one call (the fp32 state is read and
+ * written once per call), place them side by side in one buffer.
+ *   k_blk        compute dtype [L][H][kv_positions][d]: key position p of line
+ *                l, head h; positions >= nkeys are padding (finite values)
+ *   vt_blk       compute dtype [L][H][d][kv_positions]: the values, transposed
+ *   kv_positions positions of k_blk / vt_blk per (line, head): a multiple of 64,
+ *                nkeys <= kv_positions <= P (P of the workspace layout)
+ *   bias_blk     fp32 [H][I][nkeys], natural-log units: bias_blk[h][q][k] is
+ *                added to the score of query position q against key k of the
+ *                block (for TA_END: b_kq, as in the transposed problem).  It
+ *                is packed into the workspace, shifted per query by its maximum
+ *                over the block, and the shift is carried into the state's m
+ *   nkeys        keys in the block, 1 <= nkeys <= I
+ *   first        non-zero: the state is started afresh; zero: it carries earlier
+ *                blocks (folded by this entry point; states of
+ *                triangle_attn_attend_block, whose m is relative to the whole
+ *                row's bias maximum, are not to be mixed with these)
+ *   state, ws    as for triangle_attn_attend_block; this call overwrites the
+ *                workspace's packed-bias and o regions (scratch between calls)
+ * Errors: TA_ERR_NULL_PTR, TA_ERR_MISALIGNED, TA_ERR_BAD_SHAPE (nkeys or
+ * kv_positions out of range), TA_ERR_ALIAS (state or ws overlapping a block or
+ * each other), TA_ERR_WORKSPACE_TOO_SMALL; nothing is enqueued on error. */
+int triangle_attn_attend_kv_block(const ta_problem* prob, int variant, const ta_weights* w,
+                                  const void* k_blk, const void* vt_blk, int32_t kv_positions,
+                                  const float* bias_blk, int32_t nkeys, int32_t first,
+                                  float* state, void* ws, size_t ws_bytes, void* stream);
 
 /* Finish a key-block accumulation: o = O / l, sigmoid gate, output projection,
  * out as in triangle_attn_attend.  Writes the workspace's `o` region. */

@@ -153,6 +153,9 @@ triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weigh
   a.kt0 = 0;
   a.nbt = (p->I + kKeyTile - 1) / kKeyTile;  // every key
   a.redo = (int*)(base + l.redo);            // used by one-pass calls only
+  a.kv_P = l.positions;
+  a.bias_kt = l.positions / kKeyTile;
+  a.bias_shift = nullptr;
   return a;
 }
 
@@ -169,7 +172,8 @@ int enqueue(hipError_t e) { return e == hipSuccess ? TA_OK : TA_ERR_HIP; }
 int pack_bias(const ta_problem* p, int variant, const float* caller_bias, void* ws, const ta_ws_layout& l,
               hipStream_t s) {
   const float* src = variant == TA_ROWS ? caller_bias : (const float*)((char*)ws + l.bias_f32);
-  return enqueue(triattn::launch_pack_bias(src, (char*)ws + l.bias, p->I, l.positions, p->dtype, s));
+  return enqueue(triattn::launch_pack_bias(src, (char*)ws + l.bias, p->I, p->I, l.positions, l.positions, nullptr,
+                                           p->dtype, s));
 }
 
 // Shared driver of start / end / rows.
@@ -371,6 +375,57 @@ int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_wei
   if (pack && (rc = pack_bias(prob, variant, bias, ws, l, (hipStream_t)stream))) return rc;
   triattn::AttendArgs a = attend_args(prob, variant, w, nullptr, nullptr, ws, l);
   a.kt0 = key0 / kKeyTile;
+  a.nbt = (nkeys + kKeyTile - 1) / kKeyTile;
+  a.state_o = state;
+  a.state_ml = (float*)((char*)state + ob);
+  a.state_in = first ? 0 : 1;
+  a.state_out = 1;
+  return enqueue(triattn::launch_attend(a, prob->dtype, (hipStream_t)stream));
+}
+
+int triangle_attn_attend_kv_block(const ta_problem* prob, int variant, const ta_weights* w, const void* k_blk,
+                                  const void* vt_blk, int32_t kv_positions, const float* bias_blk, int32_t nkeys,
+                                  int32_t first, float* state, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_problem(prob, variant);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (k_blk == nullptr || vt_blk == nullptr || bias_blk == nullptr || state == nullptr || ws == nullptr)
+    return TA_ERR_NULL_PTR;
+  if (!aligned16(k_blk) || !aligned16(vt_blk) || !aligned16(bias_blk) || !aligned16(state) || !aligned16(ws))
+    return TA_ERR_MISALIGNED;
+  ta_ws_layout l;
+  layout_of(prob, variant, &l);
+  // a block has 1..I keys, stored at kv_positions >= nkeys positions (a multiple of the
+  // key tile, at most the workspace's P: its packed bias reuses the workspace's region)
+  if (nkeys < 1 || nkeys > prob->I || kv_positions < nkeys || kv_positions % kKeyTile != 0 ||
+      kv_positions > l.positions)
+    return TA_ERR_BAD_SHAPE;
+  if (ws_bytes < l.total) return TA_ERR_WORKSPACE_TOO_SMALL;
+  size_t ob, sb;
+  state_sizes(l, &ob, &sb);
+  const size_t es = esize(prob->dtype);
+  const size_t kv_bytes = (size_t)l.lines * kHeads * kv_positions * kHeadDim * es;
+  const Span kspan = {k_blk, kv_bytes}, vspan = {vt_blk, kv_bytes};
+  const Span bspan = {bias_blk, (size_t)kHeads * prob->I * nkeys * sizeof(float)};
+  const Span wspan = {ws, l.total}, sspan = {state, sb};
+  // state and workspace are written: neither may overlap anything else
+  const Span ins[] = {kspan, vspan, bspan};
+  for (const Span& x : ins)
+    if (overlap(x, wspan) || overlap(x, sspan)) return TA_ERR_ALIAS;
+  if ((rc = check_out_alias(prob, w, sspan, {nullptr, 0}, wspan, {nullptr, 0}))) return rc;
+  (void)hipGetLastError();
+  char* base = (char*)ws;
+  float* shift = (float*)(base + l.o);  // the o region is free during key-block calls
+  if ((rc = enqueue(triattn::launch_pack_bias(bias_blk, base + l.bias, prob->I, nkeys, l.positions, kv_positions,
+                                              shift, prob->dtype, (hipStream_t)stream))))
+    return rc;
+  triattn::AttendArgs a = attend_args(prob, variant, w, nullptr, nullptr, ws, l);
+  a.k = k_blk;
+  a.vt = vt_blk;
+  a.kv_P = kv_positions;
+  a.bias_kt = kv_positions / kKeyTile;
+  a.bias_shift = shift;
+  a.kt0 = 0;
   a.nbt = (nkeys + kKeyTile - 1) / kKeyTile;
   a.state_o = state;
   a.state_ml = (float*)((char*)state + ob);

@@ -48,6 +48,15 @@ struct AttendArgs {
   // one-pass calls: one flag per workgroup (attend_redo_flags), written by the
   // unshifted form, read by the shifted form; nullptr: the shifted form only
   int* redo;
+  // positions of the k / vt arrays (their per-line, per-head stride): P for the
+  // workspace, the block's padded key count for a caller's key block
+  int kv_P;
+  // key tiles per 32-query row of tiles in the packed bias (P / 64, or the block's)
+  int bias_kt;
+  // key-block calls on a caller's block: the per-(head, query) shift (base 2) the
+  // block's bias was packed with, [H][P]; the carried maximum is kept in true
+  // units across blocks.  nullptr: no shift
+  const float* bias_shift;
 };
 
 hipError_t launch_project(const ProjectArgs& a, int dtype, hipStream_t stream);
@@ -55,7 +64,10 @@ hipError_t launch_attend(const AttendArgs& a, int dtype, hipStream_t stream);
 // number of int32 flags launch_attend needs in AttendArgs::redo for `lines` lines of I keys
 size_t attend_redo_flags(int lines, int I);
 // tiled dst(h, j, k) = max((src[h][j][k] - max_k src[h][j][k]) * log2(e), -30000) in the
-// compute dtype; keys >= I -30000, query rows >= I zero
-hipError_t launch_pack_bias(const float* src, void* dst, int I, int P, int dtype, hipStream_t stream);
+// compute dtype for Q query rows of K keys (src row stride K); keys >= K -30000, query
+// rows >= Q zero.  dst holds P query positions by NB key positions (NB a multiple of 64).
+// shift (or nullptr) receives max_k src[h][j][k] * log2(e), [H][P] (0 past Q).
+hipError_t launch_pack_bias(const float* src, void* dst, int Q, int K, int P, int NB, float* shift, int dtype,
+                            hipStream_t stream);
 
 }  // namespace triattn

@@ -64,11 +64,11 @@ __device__ __forceinline__ int rho(int m) { return ((m >> 2) & 1) * 16 + (m >> 3
 // (lane j%32 + 32*hh holds keys 16g + 8hh + t, t = 0..7), so each chunk is one
 // contiguous per-lane load: element (j, k) with k%64 = 16g + 8hh + t sits at
 //   g*512 + (j%32 + 32*hh)*8 + t       inside a 2048-element tile.
-// P (a multiple of 128) bounds j and k.
-__device__ __forceinline__ size_t bias_tiled_index(int h, int j, int k, int P) {
+// P (a multiple of 128) bounds j, NB (P, or a key block's padded key count) bounds k.
+__device__ __forceinline__ size_t bias_tiled_index(int h, int j, int k, int P, int NB) {
   const int jb = j >> 5, jj = j & 31, kb = k >> 6, kk = k & 63;
   const int g = kk >> 4, hh = (kk >> 3) & 1, t = kk & 7;
-  return ((((size_t)h * (P >> 5) + jb) * (P >> 6) + kb) << 11) + (g << 9) + ((jj + 32 * hh) << 3) + t;
+  return ((((size_t)h * (P >> 5) + jb) * (NB >> 6) + kb) << 11) + (g << 9) + ((jj + 32 * hh) << 3) + t;
 }
 
 // ---------------------------------------------------------------- element traits
@@ -801,7 +801,9 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
 
   // line of row r (rows past the last line repeat it and are never stored)
   auto line_of = [&](int r) { return line0 + r < a.lines ? line0 + r : a.lines - 1; };
-  const size_t tok_line = (size_t)NH * P * HD;     // q, k, g, o and v^T elements per line
+  const size_t tok_line = (size_t)NH * P * HD;     // q, g and o elements per line
+  const int KP = a.kv_P;                           // positions of k / v^T
+  const size_t kv_line = (size_t)NH * KP * HD;     // k and v^T elements per line
 
   // staging: thread tid moves LDT units; slot s covers unit (s % SPR)*NT + tid of
   // row s / SPR, a K unit or a V^T unit for every thread alike (KTILE_UNITS is a
@@ -820,7 +822,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       l_off[s] = r * ROW_UNITS + row * KU + (u ^ swz<KU>(row));
     } else {
       const int ww = w - KTILE_UNITS, e = ww / VU, u = ww % VU;
-      g_off[s] = (uint32_t)(e * P + u * EPU) * sizeof(T);
+      g_off[s] = (uint32_t)(e * KP + u * EPU) * sizeof(T);
       l_off[s] = r * ROW_UNITS + KTILE_UNITS + e * VU + (u ^ swz<VU>(e));
     }
   }
@@ -830,8 +832,8 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
     for (int s = 0; s < LDT; ++s) {
       const int r = s / SPR;
       const bool is_k = (s % SPR) < SPK;
-      const T* base = is_k ? (const T*)a.k + line_of(r) * tok_line + ((size_t)h * P + kt * KT) * HD
-                           : (const T*)a.vt + line_of(r) * tok_line + (size_t)h * HD * P + kt * KT;
+      const T* base = is_k ? (const T*)a.k + line_of(r) * kv_line + ((size_t)h * KP + kt * KT) * HD
+                           : (const T*)a.vt + line_of(r) * kv_line + (size_t)h * HD * KP + kt * KT;
       sreg[s] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + g_off[s]);
     }
   };
@@ -863,8 +865,8 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
 
   // this wave's 32-query block; blocks wholly beyond I reuse the last real block
   const int jb = qb * WAVES + wave, jb_last = (I - 1) >> 5;
-  const BT* bias0 = (const BT*)a.bias + ((size_t)(jb < jb_last ? jb : jb_last) * (P >> 6) << 11);
-  const size_t bias_head = (size_t)P * P;        // elements per head; key tile stride 2048
+  const BT* bias0 = (const BT*)a.bias + ((size_t)(jb < jb_last ? jb : jb_last) * a.bias_kt << 11);
+  const size_t bias_head = (size_t)P * a.bias_kt * KT;   // elements per head; key tile stride 2048
 
   // step g = h * nbt + kt walks the key tiles kt0 + kt of every head; the step
   // after (h, kt) is (h, kt + 1), the next head's first tile, or past the end
@@ -908,20 +910,26 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       lsum[r] = 0.f;
       o[r] = zero;
       if (!UNSHIFTED && a.state_in) {
-        // carried state: shift m, sum l (held by the lower half) and unnormalised O
+        // carried state: shift m (true units), sum l (held by the lower half) and
+        // unnormalised O.  This call's scores carry its bias's shift c, so it runs
+        // with m' = m - c rounded to the compute dtype (the MFMA subtracts m'
+        // exactly); O and l are rescaled by the rounding residual 2^((m - c) - m').
         const size_t sq = ((size_t)line_of(r) * NH + h) * P + j;
         const float2 ml = *reinterpret_cast<const float2*>(a.state_ml + 2 * sq);
         const f32x4* so = reinterpret_cast<const f32x4*>(a.state_o + sq * HD + 16 * hh);
+        const float mt = ml.x - (a.bias_shift ? a.bias_shift[(size_t)h * P + j] : 0.f);
+        const float me = (float)(T)mt;
+        const float alpha = fast_exp2(mt - me);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const f32x4 v = so[q4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) o[r][4 * q4 + t] = v[t];
+          for (int t = 0; t < 4; ++t) o[r][4 * q4 + t] = v[t] * alpha;
         }
-        m[r] = ml.x;
-        lsum[r] = hh == 0 ? ml.y : 0.f;
-        qm[r] = unit_frag<T>(hh == 0 ? -ml.x : 0.f);
-        mact[r] = __builtin_amdgcn_ballot_w64(ml.x != 0.f) != 0;
+        m[r] = me;
+        lsum[r] = hh == 0 ? ml.y * alpha : 0.f;
+        qm[r] = unit_frag<T>(hh == 0 ? -me : 0.f);
+        mact[r] = __builtin_amdgcn_ballot_w64(me != 0.f) != 0;
       }
     }
 
@@ -1097,7 +1105,8 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
         f32x4* so = reinterpret_cast<f32x4*>(a.state_o + sq * HD + 16 * hh);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) so[q4] = f32x4{o[r][4 * q4], o[r][4 * q4 + 1], o[r][4 * q4 + 2], o[r][4 * q4 + 3]};
-        if (hh == 0) *reinterpret_cast<float2*>(a.state_ml + 2 * sq) = make_float2(m[r], lt);
+        const float mt = m[r] + (a.bias_shift ? a.bias_shift[(size_t)h * P + j] : 0.f);
+        if (hh == 0) *reinterpret_cast<float2*>(a.state_ml + 2 * sq) = make_float2(mt, lt);
       }
       continue;
     }
@@ -1130,19 +1139,22 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
 }
 
 // ================================================================ K2: bf16 one-pass form
-// The bf16 unshifted form, rebuilt for the issue rates of gfx950: v_exp_f32 issues
+// The bf16 unshifted form, built for the issue rates of gfx950: v_exp_f32 issues
 // about once per 9 cycles per SIMD and overlaps poorly with the matrix core, plain
 // VALU work overlaps it fully, and a wave waits for a load only where it uses it.
-// So, per key tile of 64 keys and two rows:
-//  * the next tile's bias and K/V loads are issued at the top of the tile and
-//    consumed at its end (the compiler may not sink them: a scheduling fence);
-//  * row sums come from the matrix core (v_mfma_f32_16x16x32_bf16 with a 0/1
-//    operand, below) instead of 32 dot products on the VALU;
-//  * the tile runs as four chunks of 32 keys x 32 queries (row r, half st): the
-//    scores of chunk c+1 and the P.V and row-sum products of chunk c-1 go to the
-//    matrix core while the VALU exponentiates chunk c;
-//  * the bias products of the next tile (selector MFMAs) run in the tile's last
-//    phase, once the current tile's scores no longer need their registers.
+//  * The key loop is one continuous pipeline of chunks of 32 keys x 32 queries
+//    (key tile kt, row r, half st: chunk 4 kt + 2 r + st).  While the VALU
+//    exponentiates chunk c, the matrix core computes the scores of chunk c + 1 and
+//    the P.V and row-sum products of chunk c - 1, across key-tile boundaries, so a
+//    tile has no start-up or drain phase (only a head's first and last tiles do).
+//  * K/V tiles go through a ring of three LDS slots: tile t + 2 is loaded at the
+//    top of tile t and stored into its slot at the end, so tile t + 1 is already in
+//    LDS while tile t runs (its first scores are computed in tile t's last phase).
+//  * The next tile's bias is loaded at the top of the tile; its selector products
+//    run in the tile's last two phases, once the current scores no longer need
+//    their registers.
+//  * Row sums come from the matrix core (v_mfma_f32_16x16x32_bf16 with a 0/1
+//    operand, below) instead of 32 dot products per tile on the VALU.
 // Semantics, workgroup grid, redo flags and epilogue are those of tri_attend's
 // unshifted form.
 
@@ -1180,12 +1192,13 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
   constexpr int KTILE_UNITS = KT * KU;
   constexpr int VTILE_UNITS = HD * VU;
   constexpr int ROW_UNITS = KTILE_UNITS + VTILE_UNITS;
-  constexpr int STAGE_UNITS = ROWS * ROW_UNITS;
+  constexpr int STAGE_UNITS = ROWS * ROW_UNITS;   // one key tile of both rows: 16 KiB
+  constexpr int NSLOT = 3;                        // LDS ring
   constexpr int LDT = STAGE_UNITS / NT;           // 16-B units staged per thread per tile
   constexpr int EPU = 8;                          // bf16 elements per 16-B unit
   constexpr int QBW = 32 * WAVES;                 // queries per workgroup
   static_assert(STAGE_UNITS % NT == 0 && KTILE_UNITS % NT == 0 && VTILE_UNITS % NT == 0, "staging split");
-  __shared__ u32x4 kv_lds[2][STAGE_UNITS];
+  __shared__ u32x4 kv_lds[NSLOT * STAGE_UNITS];
   __shared__ int redo_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, lr = lane & 31;
@@ -1196,11 +1209,11 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
   map_block(a.xcd_mode, blockIdx.x, n_lg, a.nqb, lg, qb);
   const int line0 = lg * ROWS;
   const int j = qb * QBW + wave * 32 + lr;        // this lane's query
-  const int kt0 = a.kt0, nbt = a.nbt;
+  const int kt0 = a.kt0, nbt = a.nbt;             // nbt >= 1 (one-pass calls)
   auto line_of = [&](int r) { return line0 + r < a.lines ? line0 + r : a.lines - 1; };
   const size_t tok_line = (size_t)NH * P * HD;
 
-  // K/V staging: as in tri_attend (each slot a scalar base plus a per-lane offset)
+  // K/V staging (as in tri_attend: each slot a scalar base plus a per-lane offset)
   constexpr int SPR = ROW_UNITS / NT;
   constexpr int SPK = KTILE_UNITS / NT;
   uint32_t g_off[LDT];
@@ -1229,11 +1242,16 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       sreg[s] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + g_off[s]);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int slot) {
+    u32x4* dst = kv_lds + slot * STAGE_UNITS;
 #pragma unroll
-    for (int s = 0; s < LDT; ++s) kv_lds[buf][l_off[s]] = sreg[s];
+    for (int s = 0; s < LDT; ++s) dst[l_off[s]] = sreg[s];
   };
-  auto load_bias = [&](const BT* btile, bfrag (&b)[4]) {
+  const int jb = qb * WAVES + wave, jb_last = (I - 1) >> 5;
+  const BT* bias0 = (const BT*)a.bias + ((size_t)(jb < jb_last ? jb : jb_last) * a.bias_kt << 11);
+  const size_t bias_head = (size_t)P * a.bias_kt * KT;
+  auto load_bias = [&](int h, int kt, bfrag (&b)[4]) {
+    const BT* btile = bias0 + h * bias_head + ((size_t)kt << 11);
 #pragma unroll
     for (int g = 0; g < 4; ++g) b[g] = *reinterpret_cast<const bfrag*>(btile + g * 512 + lane * 8);
   };
@@ -1249,39 +1267,55 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
   const frag rsel = rowsum_selector(lane);
   const int rs_src = rowsum_lane(lr);
   const f32x16 zero = {};
-  auto bias_scores = [&](const bfrag (&b)[4], f32x16 (&sb)[2]) {
-#pragma unroll
-    for (int st = 0; st < 2; ++st) sb[st] = mma(esel[0], b[2 * st], zero);
-#pragma unroll
-    for (int st = 0; st < 2; ++st) sb[st] = mma(esel[1], b[2 * st + 1], sb[st]);
+  // selector products: the bias of keys 32 st .. 32 st + 31 of a tile in the score layout
+  auto bias_scores = [&](const bfrag (&b)[4], int st) {
+    return mma(esel[1], b[2 * st + 1], mma(esel[0], b[2 * st], zero));
   };
 
-  const int jb = qb * WAVES + wave, jb_last = (I - 1) >> 5;
-  const BT* bias0 = (const BT*)a.bias + ((size_t)(jb < jb_last ? jb : jb_last) * (P >> 6) << 11);
-  const size_t bias_head = (size_t)P * P;
-  auto next_tile = [&](int h, int kt, int& hn, int& ktn) {
-    hn = h;
-    ktn = kt + 1;
-    if (ktn == nbt) {
-      hn = h + 1;
-      ktn = 0;
+  // steps: g = h * nbt + kt walks the key tiles of every head in order; (h1, kt1)
+  // is step g + 1 (its bias is loaded during step g) and (h2, kt2) step g + 2 (its
+  // K/V); past the last step both stay on the last one (loaded, unused)
+  auto advance = [&](int& hx, int& ktx) {
+    if (++ktx == nbt) {
+      ktx = 0;
+      ++hx;
     }
-    if (hn == NH) {
-      hn = NH - 1;
-      ktn = nbt - 1;
+    if (hx == NH) {
+      hx = NH - 1;
+      ktx = nbt - 1;
     }
   };
+  int h1 = 0, kt1 = 0, h2 = 0, kt2 = 0;
+  int slot_cur = 0, slot_nxt = 1, slot_wr = 2;    // ring slots of steps g, g + 1, g + 2
   if (tid == 0) redo_flag = 0;
   bool bad = false;
   f32x16 sbias[2];
   {
     bfrag b0[4];
-    load_bias(bias0 + ((size_t)kt0 << 11), b0);
+    load_bias(0, kt0, b0);
     load_tile(0, kt0);
     store_tile(0);
-    bias_scores(b0, sbias);
+    advance(h2, kt2);
+    load_tile(h2, kt0 + kt2);
+    store_tile(1);
+    advance(h2, kt2);
+    advance(h1, kt1);
+    sbias[0] = bias_scores(b0, 0);
+    sbias[1] = bias_scores(b0, 1);
     __syncthreads();
   }
+
+  // chunk c = 2 r + st of a tile: row r, keys 32 st .. 32 st + 31
+  auto kfr = [&](const u32x4* lds, int c, frag (&kf)[2]) {
+    const u32x4* kl = lds + (c >> 1) * ROW_UNITS;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) kf[cc] = lds_frag<T, KU>(kl, 32 * (c & 1) + rho(lr), 2 * cc + hh);
+  };
+  auto vfr = [&](const u32x4* lds, int c, frag (&vf)[2]) {
+    const u32x4* vl = lds + (c >> 1) * ROW_UNITS + KTILE_UNITS;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) vf[cc] = lds_frag<T, VU>(vl, rho(lr), 4 * (c & 1) + 2 * hh + cc);
+  };
 
 #pragma unroll 1
   for (int h = 0; h < NH; ++h) {
@@ -1296,33 +1330,31 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       o[r] = zero;
       lacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    auto score = [&](int c, const frag (&kf)[2]) {
+      const int r = c >> 1;
+      return mma(kf[1], qf[r][1], mma(kf[0], qf[r][0], sbias[c & 1]));
+    };
+    auto pv = [&](int c, const frag (&vf)[2], const frag (&pf)[2]) {
+      const int r = c >> 1;
+      o[r] = mma(vf[0], pf[0], o[r]);
+      lacc[r] = mma16(rsel, pf[0], lacc[r]);
+      o[r] = mma(vf[1], pf[1], o[r]);
+      lacc[r] = mma16(rsel, pf[1], lacc[r]);
+    };
+    // carried from one tile to the next: the scores of the next tile's chunk 0,
+    // and P and the V^T fragments of this tile's chunk 3
+    f32x16 s_first;
+    frag pf_last[2], vf_last[2];
 
-    auto tile = [&](int kt, auto first_tag) {
-      constexpr bool FIRST = decltype(first_tag)::value;
-      const int g = h * nbt + kt, buf = g & 1;
-      int hn, ktn;
-      next_tile(h, kt, hn, ktn);
-      // the next tile's bias and K/V: issued here, used in the last two phases
+    auto tile = [&](auto first_tag, auto last_tag) {
+      constexpr bool FIRST = decltype(first_tag)::value;   // first key tile of the head
+      constexpr bool LAST = decltype(last_tag)::value;     // last key tile of the head
       bfrag bias_nx[4];
-      load_bias(bias0 + hn * bias_head + ((size_t)(kt0 + ktn) << 11), bias_nx);
-      load_tile(hn, kt0 + ktn);
+      load_bias(h1, kt0 + kt1, bias_nx);
+      load_tile(h2, kt0 + kt2);
       TA_FENCE();
-      const u32x4* lds = kv_lds[buf];
-      auto kfr = [&](int c, frag (&kf)[2]) {
-        const u32x4* kl = lds + (c >> 1) * ROW_UNITS;
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) kf[cc] = lds_frag<T, KU>(kl, 32 * (c & 1) + rho(lr), 2 * cc + hh);
-      };
-      auto vfr = [&](int c, frag (&vf)[2]) {
-        const u32x4* vl = lds + (c >> 1) * ROW_UNITS + KTILE_UNITS;
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) vf[cc] = lds_frag<T, VU>(vl, rho(lr), 4 * (c & 1) + 2 * hh + cc);
-      };
-      auto score = [&](int c, const frag (&kf)[2]) {
-        const int r = c >> 1;
-        f32x16 s = mma(kf[0], qf[r][0], sbias[c & 1]);
-        return mma(kf[1], qf[r][1], s);
-      };
+      const u32x4* cur = kv_lds + slot_cur * STAGE_UNITS;
+      const u32x4* nxt = kv_lds + slot_nxt * STAGE_UNITS;
       float mxr[ROWS] = {-INFINITY, -INFINITY};
       auto expo = [&](int c, const f32x16& s, frag (&pf)[2]) {
         if constexpr (FIRST) {
@@ -1339,59 +1371,57 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
           pf[cc] = to_frag<T>(p);
         }
       };
-      auto pv = [&](int c, const frag (&vf)[2], const frag (&pf)[2]) {
-        const int r = c >> 1;
-        o[r] = mma(vf[0], pf[0], o[r]);
-        lacc[r] = mma16(rsel, pf[0], lacc[r]);
-        o[r] = mma(vf[1], pf[1], o[r]);
-        lacc[r] = mma16(rsel, pf[1], lacc[r]);
-      };
-      frag kf0[2], kf1[2], kf2[2], kf3[2], vf0[2], vf1[2], vf2[2], vf3[2];
-      frag pf0[2], pf1[2], pf2[2], pf3[2];
-      // phase 0: scores of chunk 0
-      kfr(0, kf0);
-      kfr(1, kf1);
-      const f32x16 s0 = score(0, kf0);
-      TA_FENCE();
-      // phase 1: scores of chunk 1 | exponentials of chunk 0
-      kfr(2, kf2);
-      vfr(0, vf0);
-      const f32x16 s1 = score(1, kf1);
-      expo(0, s0, pf0);
+      frag kfa[2], kfb[2], vfa[2], vfb[2], pf0[2], pf1[2], pf2[2];
+      if constexpr (FIRST) {                       // fill: the scores of chunk 0
+        kfr(cur, 0, kfa);
+        s_first = score(0, kfa);
+        TA_FENCE();
+      }
+      // phase 0: scores of chunk 1, P.V of the previous tile's chunk 3 | exponentials of chunk 0
+      kfr(cur, 1, kfa);
+      vfr(cur, 0, vfa);
+      const f32x16 s1 = score(1, kfa);
+      if constexpr (!FIRST) pv(3, vf_last, pf_last);
+      expo(0, s_first, pf0);
       TA_SGB(0x100, 4);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 12); }
+      for (int i = 0; i < (FIRST ? 2 : 6); ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, FIRST ? 12 : 4); }
       TA_FENCE();
-      // phase 2: scores of chunk 2, P.V of chunk 0 | exponentials of chunk 1
-      kfr(3, kf3);
-      vfr(1, vf1);
-      const f32x16 s2 = score(2, kf2);
-      pv(0, vf0, pf0);
+      // phase 1: scores of chunk 2, P.V of chunk 0 | exponentials of chunk 1
+      kfr(cur, 2, kfb);
+      vfr(cur, 1, vfb);
+      const f32x16 s2 = score(2, kfb);
+      pv(0, vfa, pf0);
       expo(1, s1, pf1);
       TA_SGB(0x100, 4);
 #pragma unroll
       for (int i = 0; i < 6; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 4); }
       TA_FENCE();
-      // phase 3: scores of chunk 3, P.V of chunk 1 | exponentials of chunk 2
-      vfr(2, vf2);
-      const f32x16 s3 = score(3, kf3);
-      pv(1, vf1, pf1);
+      // phase 2: scores of chunk 3, P.V of chunk 1, bias products of the next
+      // tile's first half | exponentials of chunk 2
+      kfr(cur, 3, kfa);
+      vfr(cur, 2, vfa);
+      const f32x16 s3 = score(3, kfa);
+      pv(1, vfb, pf1);
+      sbias[0] = bias_scores(bias_nx, 0);
       expo(2, s2, pf2);
-      TA_SGB(0x100, 2);
-#pragma unroll
-      for (int i = 0; i < 6; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 4); }
-      TA_FENCE();
-      // phase 4: P.V of chunk 2, the next tile's bias products | exponentials of chunk 3
-      vfr(3, vf3);
-      pv(2, vf2, pf2);
-      bias_scores(bias_nx, sbias);
-      expo(3, s3, pf3);
-      TA_SGB(0x100, 2);
+      TA_SGB(0x100, 4);
 #pragma unroll
       for (int i = 0; i < 8; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 3); }
       TA_FENCE();
-      // phase 5: P.V of chunk 3; the next tile's K/V into the other buffer
-      pv(3, vf3, pf3);
+      // phase 3: scores of the next tile's chunk 0, P.V of chunk 2, bias products of
+      // the next tile's second half | exponentials of chunk 3
+      if constexpr (!LAST) kfr(nxt, 0, kfb);
+      vfr(cur, 3, vf_last);
+      if constexpr (!LAST) s_first = score(0, kfb);
+      pv(2, vfa, pf2);
+      sbias[1] = bias_scores(bias_nx, 1);
+      expo(3, s3, pf_last);
+      TA_SGB(0x100, LAST ? 2 : 4);
+#pragma unroll
+      for (int i = 0; i < (LAST ? 6 : 8); ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 3); }
+      TA_FENCE();
+      if constexpr (LAST) pv(3, vf_last, pf_last);  // drain: the head's last chunk
       if constexpr (FIRST) {
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
@@ -1399,12 +1429,23 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
           bad = bad || mx > FIRST_LIMIT || mx < -FIRST_LIMIT;
         }
       }
-      store_tile(buf ^ 1);
+      store_tile(slot_wr);                          // K/V of step g + 2
       __syncthreads();
+      advance(h1, kt1);
+      advance(h2, kt2);
+      const int s0 = slot_cur;
+      slot_cur = slot_nxt;
+      slot_nxt = slot_wr;
+      slot_wr = s0;
     };
 
-    if (nbt > 0) tile(0, std::true_type{});
-    for (int kt = 1; kt < nbt; ++kt) tile(kt, std::false_type{});
+    if (nbt == 1) {
+      tile(std::true_type{}, std::true_type{});
+    } else {
+      tile(std::true_type{}, std::false_type{});
+      for (int kt = 1; kt < nbt - 1; ++kt) tile(std::false_type{}, std::false_type{});
+      tile(std::false_type{}, std::true_type{});
+    }
 
     // ---- finish head h: row sums, 1/l, gate; o^T (e = 16*hh + i) to the workspace
 #pragma unroll
@@ -1429,39 +1470,43 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
   const bool redo = redo_flag != 0;
   if (tid == 0) a.redo[blockIdx.x] = redo ? 1 : 0;
   if (redo) return;
-  static_assert(2 * STAGE_UNITS >= CZ * CZ * 2 / 16, "W_o must fit in the K/V staging area");
-  out_projection<T, ROWS, NT>(a, line0, j, hh, lr, &kv_lds[0][0]);
+  static_assert(NSLOT * STAGE_UNITS >= CZ * CZ * 2 / 16, "W_o must fit in the K/V staging area");
+  out_projection<T, ROWS, NT>(a, line0, j, hh, lr, kv_lds);
 }
 
-// Bias pack: natural-log fp32 bias [H][I][I] (from K1 or the caller) into the
-// attention kernel's tiled layout (fp16 for bf16 problems, fp32 for fp32).  Each query row is
-// shifted by its own maximum before the base-2 scale and the rounding: the
-// softmax over keys does not change under a per-query shift, and after it the
-// entries that carry the weight sit near 0, where a bf16 rounding error is
-// smallest.  Keys >= I get MASKED; values below MASKED (e.g. -inf, a masked
-// key) are raised to it; padded query rows I..(I rounded up to 32)-1 get 0.
+// Bias pack: natural-log fp32 bias [H][Q][K] (from K1 or the caller: Q query rows,
+// K keys; Q = K = I for a whole problem, K = a key block's size for a block) into
+// the attention kernel's tiled layout (fp16 for bf16 problems, fp32 for fp32) of P
+// query positions by NB key positions.  Each query row is shifted by its own
+// maximum before the base-2 scale and the rounding: the softmax over keys does not
+// change under a per-query shift, and after it the entries that carry the weight
+// sit near 0, where the rounding error of the compute dtype is smallest; the shift
+// (base 2) goes to `shift` when the caller needs it (key blocks).  Keys >= K get
+// MASKED; values below MASKED (e.g. -inf, a masked key) are raised to it; padded
+// query rows Q..(Q rounded up to 32)-1 get 0 and a zero shift.
 template <typename BT>
 __global__ void __launch_bounds__(NTHREADS) tri_pack_bias(const float* __restrict__ src, BT* __restrict__ dst,
-                                                          int I, int P, int rows_pad) {
+                                                          int Q, int K, int P, int NB, int rows_pad,
+                                                          float* __restrict__ shift) {
   __shared__ float red[NTHREADS / 64];
   for (int r = blockIdx.x; r < NH * rows_pad; r += gridDim.x) {
     const int h = r / rows_pad, j = r % rows_pad;
-    const float* s = src + ((size_t)h * I + j) * I;
+    const float* s = src + ((size_t)h * Q + j) * K;
     // four consecutive keys per thread: one 16-B read when the row is 16-B aligned,
     // and one contiguous run of the tiled layout to write
     const bool vec = (reinterpret_cast<uintptr_t>(s) & 15) == 0;
     auto load4 = [&](int k0, float (&v)[4]) {
-      if (vec && k0 + 3 < I) {
+      if (vec && k0 + 3 < K) {
         const float4 f = *reinterpret_cast<const float4*>(s + k0);
         v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
       } else {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = k0 + t < I ? s[k0 + t] : -INFINITY;
+        for (int t = 0; t < 4; ++t) v[t] = k0 + t < K ? s[k0 + t] : -INFINITY;
       }
     };
     float mx = -INFINITY;
-    if (j < I)
-      for (int c = threadIdx.x; c < ((I + 3) >> 2); c += NTHREADS) {
+    if (j < Q)
+      for (int c = threadIdx.x; c < ((K + 3) >> 2); c += NTHREADS) {
         float v[4];
         load4(c << 2, v);
         mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
@@ -1471,18 +1516,19 @@ __global__ void __launch_bounds__(NTHREADS) tri_pack_bias(const float* __restric
     __syncthreads();
     mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();  // red is reused by the next row
-    for (int c = threadIdx.x; c < (P >> 2); c += NTHREADS) {
+    if (shift != nullptr && threadIdx.x == 0) shift[(size_t)h * P + j] = j < Q ? mx * LOG2E : 0.f;
+    for (int c = threadIdx.x; c < (NB >> 2); c += NTHREADS) {
       const int k0 = c << 2;
       float v[4] = {0.f, 0.f, 0.f, 0.f};
-      if (j < I) load4(k0, v);
+      if (j < Q) load4(k0, v);
       BT out4[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        float x = k0 + t < I ? (j < I ? (v[t] - mx) * LOG2E : 0.f) : MASKED;
+        float x = k0 + t < K ? (j < Q ? (v[t] - mx) * LOG2E : 0.f) : MASKED;
         x = x < MASKED ? MASKED : x;  // NaN stays NaN
         out4[t] = (BT)x;
       }
-      BT* d = dst + bias_tiled_index(h, j, k0, P);
+      BT* d = dst + bias_tiled_index(h, j, k0, P, NB);
       if constexpr (sizeof(BT) == 2) {
         uint2 w;
         __builtin_memcpy(&w, out4, 8);
@@ -1540,15 +1586,16 @@ hipError_t launch_project(const ProjectArgs& a, int dtype, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_pack_bias(const float* src, void* dst, int I, int P, int dtype, hipStream_t stream) {
-  const int rows_pad = (I + 31) & ~31;
+hipError_t launch_pack_bias(const float* src, void* dst, int Q, int K, int P, int NB, float* shift, int dtype,
+                            hipStream_t stream) {
+  const int rows_pad = (Q + 31) & ~31;
   int grid = NH * rows_pad < 8 * cu_count() ? NH * rows_pad : 8 * cu_count();
   if (dtype == 1)
     hipLaunchKernelGGL(tri_pack_bias<_Float16>, dim3((unsigned)grid), dim3(NTHREADS), 0, stream, src,
-                       (_Float16*)dst, I, P, rows_pad);
+                       (_Float16*)dst, Q, K, P, NB, rows_pad, shift);
   else
     hipLaunchKernelGGL(tri_pack_bias<float>, dim3((unsigned)grid), dim3(NTHREADS), 0, stream, src,
-                       (float*)dst, I, P, rows_pad);
+                       (float*)dst, Q, K, P, NB, rows_pad, shift);
   return hipGetLastError();
 }
 

@@ -40,13 +40,13 @@ def layout(lib, p, variant):
 
 def test_exports_match_header(lib):
     names = ta.header_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror(lib):
-    assert lib.triangle_attn_abi_version() == 4
+    assert lib.triangle_attn_abi_version() == 5
     for code in range(0, -12, -1):
         msg = lib.triangle_attn_strerror(code).decode()
         assert msg and msg != "unknown error code"
@@ -215,6 +215,33 @@ def test_block_rejects(lib):
     assert fin(ctypes.byref(p), ta.TA_START, ctypes.byref(w), None, A + 100 * MB, A + 200 * MB, lay.total, None) == -1
     assert fin(ctypes.byref(p), ta.TA_START, ctypes.byref(w), A + 300 * MB, A + 200 * MB + 512, A + 200 * MB,
                lay.total, None) == -7   # out inside the workspace
+
+
+def test_kv_block_rejects(lib):
+    """The ring step on caller-held blocks: shapes, pointers, alignment and overlaps."""
+    p = prob(I=200)                          # P = 256
+    w = weights()
+    rc, lay = layout(lib, p, ta.TA_START)
+    f = lib.triangle_attn_attend_kv_block
+    K, V, B, ST, WS = A + 400 * MB, A + 450 * MB, A + 500 * MB, A + 300 * MB, A + 200 * MB
+
+    def call(k=K, vt=V, npos=128, bias=B, nkeys=100, first=1, st=ST, ws=WS, wsb=lay.total, variant=ta.TA_START):
+        return f(ctypes.byref(p), variant, ctypes.byref(w), k, vt, npos, bias, nkeys, first, st, ws, wsb, None)
+
+    assert call() != -2 and call() != -1     # (the valid shape reaches the launch; no GPU here)
+    assert call(nkeys=0) == -2
+    assert call(nkeys=201) == -2             # more keys than I
+    assert call(nkeys=129) == -2             # more keys than positions
+    assert call(npos=96) == -2               # positions not a multiple of 64
+    assert call(npos=320) == -2              # positions past the workspace's P
+    assert call(k=None) == -1 and call(vt=None) == -1 and call(bias=None) == -1
+    assert call(st=None) == -1 and call(ws=None) == -1
+    assert call(k=K + 8) == -6 and call(bias=B + 4) == -6 and call(st=ST + 4) == -6
+    assert call(wsb=lay.total - 1) == -5
+    assert call(st=K + 4096) == -7           # state over the key block
+    assert call(k=WS + 4096) == -7           # key block inside the workspace
+    assert call(bias=ST + 256) == -7         # bias block inside the state
+    assert call(variant=9) == -9
 
 
 # ----------------------------------------------------------------------------------------- AAQ codec
