@@ -70,7 +70,9 @@ enum {
   TA_ERR_HIP = -8,               /* a kernel launch was rejected by the HIP runtime */
   TA_ERR_BAD_VARIANT = -9,
   TA_ERR_BAD_EPS = -10,          /* ln_eps not finite and > 0 */
-  TA_ERR_BAD_GROUP = -11         /* AAQ group not A, B or C (include/aaq.h) */
+  TA_ERR_BAD_GROUP = -11,        /* AAQ group not A, B or C (include/aaq.h) */
+  TA_ERR_TOO_LARGE = -12         /* the problem needs more than the static workspace of
+                                    triangle_attn_start_noalloc */
 };
 
 /* Problem description (host memory). */
@@ -257,6 +259,25 @@ int triangle_attn_attend_kv_block(const ta_problem* prob, int variant, const ta_
                                   const void* k_blk, const void* vt_blk, int32_t kv_positions,
                                   const float* bias_blk, int32_t nkeys, int32_t first,
                                   float* state, void* ws, size_t ws_bytes, void* stream);
+
+/* triangle_attn_start without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid it).  The workspace is a static
+ * device array of TRIATTN_NOALLOC_SCRATCH_BYTES (256 MiB) that every GPU the
+ * library runs on holds until the process ends; its address is looked up once
+ * per device, on the first call there.  Problems whose workspace (the layout of
+ * triangle_attn_workspace_layout for TA_START) exceeds it are rejected with
+ * TA_ERR_TOO_LARGE before anything is enqueued: I up to about 400 in bf16, about
+ * 290 in fp32.  All calls on one GPU share that GPU's array and leave their
+ * intermediates in it: calls that overlap in time on one GPU (several host
+ * threads, or several streams without ordering between the calls) race and
+ * give undefined results; calls ordered on one stream are safe.  Nothing needs
+ * to start at zero: every region the kernels read is written earlier in the same
+ * call.  Other arguments and errors as for triangle_attn_start (TA_ERR_HIP also
+ * when the array's address cannot be obtained). */
+#define TRIATTN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int triangle_attn_start_noalloc(const ta_problem* prob, const ta_weights* w, const void* z,
+                                void* out, void* stream);
 
 /* Finish a key-block accumulation: o = O / l, sigmoid gate, output projection,
  * out as in triangle_attn_attend.  Writes the workspace's `o` region. */

@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/aaq.h"
@@ -201,6 +203,29 @@ int run_full(const ta_problem* p, int variant, const ta_weights* w, const void* 
   return enqueue(triattn::launch_attend(aa, p->dtype, s));
 }
 
+// Static workspace of triangle_attn_start_noalloc: one copy per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: only the per-device address from hipGetSymbolAddress is ever used.
+static __device__ __align__(256) unsigned char scratch[TRIATTN_NOALLOC_SCRATCH_BYTES];
+static_assert(sizeof(scratch) == TRIATTN_NOALLOC_SCRATCH_BYTES, "scratch size");
+
+// Address of `scratch` on the current device, looked up once per device (with that
+// device current, as this function is called).  nullptr if the runtime fails.
+void* scratch_on_current_device() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,6 +246,8 @@ const char* triangle_attn_strerror(int code) {
     case TA_ERR_BAD_VARIANT: return "unknown variant";
     case TA_ERR_BAD_EPS: return "ln_eps must be finite and positive";
     case TA_ERR_BAD_GROUP: return "AAQ group must be AAQ_GROUP_A, _B or _C";
+    case TA_ERR_TOO_LARGE:
+      return "problem needs more than the 256 MiB static workspace of triangle_attn_start_noalloc";
     default: return "unknown error code";
   }
 }
@@ -236,6 +263,20 @@ int triangle_attn_workspace_layout(const ta_problem* prob, int variant, ta_ws_la
 int triangle_attn_start(const ta_problem* prob, const ta_weights* w, const void* z, void* out, void* ws,
                         size_t ws_bytes, void* stream) {
   return run_full(prob, TA_START, w, z, nullptr, out, ws, ws_bytes, stream);
+}
+
+int triangle_attn_start_noalloc(const ta_problem* prob, const ta_weights* w, const void* z, void* out,
+                                void* stream) {
+  int rc = check_problem(prob, TA_START);
+  if (rc) return rc;
+  ta_ws_layout l;
+  layout_of(prob, TA_START, &l);
+  if (l.total > TRIATTN_NOALLOC_SCRATCH_BYTES) return TA_ERR_TOO_LARGE;
+  if ((rc = check_weights(w))) return rc;
+  if (z == nullptr || out == nullptr) return TA_ERR_NULL_PTR;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return TA_ERR_HIP;
+  return run_full(prob, TA_START, w, z, nullptr, out, ws, TRIATTN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int triangle_attn_end(const ta_problem* prob, const ta_weights* w, const void* z, void* out, void* ws,

@@ -76,6 +76,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "triangle_attn_strerror": ([i32], ctypes.c_char_p),
         "triangle_attn_workspace_layout": ([P, i32, L], i32),
         "triangle_attn_start": ([P, W, vp, vp, vp, sz, vp], i32),
+        "triangle_attn_start_noalloc": ([P, W, vp, vp, vp], i32),
         "triangle_attn_end": ([P, W, vp, vp, vp, sz, vp], i32),
         "triangle_attn_start_rows": ([P, W, vp, vp, vp, vp, sz, vp], i32),
         "triangle_attn_pair_bias": ([P, W, vp, ctypes.c_int32, vp, vp], i32),
@@ -212,6 +213,20 @@ def triangle_attn_pair_bias(z_rows, weights, row0=0, bias=None, I=None, stream=N
         ctypes.byref(problem(I, R, z_rows.dtype, eps)), ctypes.byref(weights_struct(weights, z_rows.dtype)),
         _ptr(z_rows), int(row0), _ptr(bias), _stream(stream)))
     return bias
+
+
+def triangle_attn_start_noalloc(z, weights, out, stream=None, eps=1e-5):
+    """triangle_attn_start on the library's static workspace (no workspace argument;
+    the caller passes the output, so nothing is allocated here either)."""
+    _dev(z, "z")
+    I = z.shape[0]
+    if z.shape != (I, I, C_Z):
+        raise ValueError(f"z must be [I][I][{C_Z}], got {tuple(z.shape)}")
+    _dev(out, "out", z.dtype)
+    _check(load_library().triangle_attn_start_noalloc(
+        ctypes.byref(problem(I, I, z.dtype, eps)), ctypes.byref(weights_struct(weights, z.dtype)), _ptr(z),
+        _ptr(out), _stream(stream)))
+    return out
 
 
 def triangle_attn_project(z, weights, variant="start", ws=None, stream=None, eps=1e-5):

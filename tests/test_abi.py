@@ -40,14 +40,14 @@ def layout(lib, p, variant):
 
 def test_exports_match_header(lib):
     names = ta.header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror(lib):
     assert lib.triangle_attn_abi_version() == 5
-    for code in range(0, -12, -1):
+    for code in range(0, -13, -1):
         msg = lib.triangle_attn_strerror(code).decode()
         assert msg and msg != "unknown error code"
     assert lib.triangle_attn_strerror(-99).decode() == "unknown error code"
@@ -215,6 +215,21 @@ def test_block_rejects(lib):
     assert fin(ctypes.byref(p), ta.TA_START, ctypes.byref(w), None, A + 100 * MB, A + 200 * MB, lay.total, None) == -1
     assert fin(ctypes.byref(p), ta.TA_START, ctypes.byref(w), A + 300 * MB, A + 200 * MB + 512, A + 200 * MB,
                lay.total, None) == -7   # out inside the workspace
+
+
+def test_noalloc_rejects(lib):
+    """The static-workspace entry point validates before it looks up its array (no GPU here)."""
+    w = weights()
+    f = lib.triangle_attn_start_noalloc
+    call = lambda p, z=A, out=A + 100 * MB, ww=w: f(ctypes.byref(p), None if ww is None else ctypes.byref(ww), z,
+                                                   out, None)
+    assert call(prob(I=512)) == -12                     # workspace past 256 MiB
+    assert call(prob(I=300, dtype=ta.TA_F32)) == -12
+    assert call(prob(I=64, rows=32)) == -2
+    assert call(prob(I=64), ww=None) == -1
+    assert call(prob(I=64), z=None) == -1
+    assert call(prob(I=64), out=None) == -1
+    assert f(None, ctypes.byref(w), A, A, None) == -1
 
 
 def test_kv_block_rejects(lib):
