@@ -480,18 +480,22 @@ def summarize_sq(run_dir, workload):
     lines.append(f"#   python3 bench.py --summarize-sq $O --workload {workload}")
     lines.append(f"# kernel_sha={kernel_sha()}")
     lines.append("# normalisation: per SIMD, counter / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs);"
-                 " SQ_ACTIVE_INST_* are in quad-cycles (x 4)")
+                 " SQ_ACTIVE_INST_* are in quad-cycles (x 4), SQ_WAVE_CYCLES and SQ_WAIT_* in quad-cycles too")
     lines += [f"{k:28s} {v:18.1f}" for k, v in sorted(c.items())]
     lines += [
         f"dispatches_per_pass        {len(durations)}",
         f"avg_dispatch_ms            {dur * 1e3:.4f}",
         f"effective_clock_ghz        {xcd_cycles / dur / 1e9:.3f}   (GRBM_GUI_ACTIVE / 8 / dispatch time)",
         f"mfma_busy                  {mfma:.4f}   (SQ_VALU_MFMA_BUSY_CYCLES per SIMD-cycle)",
-        f"valu_active                {valu:.4f}   (4 x SQ_ACTIVE_INST_VALU per SIMD-cycle; MFMA issue included)",
+        f"valu_active                {valu:.4f}   (4 x SQ_ACTIVE_INST_VALU, VALU cycles summed over the waves, per "
+        "SIMD-cycle; MFMA issue included)",
         f"mfma_valu_coexec           {coex:.4f}   (SQ_VALU_MFMA_COEXEC_CYCLES per SIMD-cycle)",
         f"mfma_or_valu               {mfma + valu - coex:.4f}",
-        f"wave_wait_inst_any         {c['SQ_WAIT_INST_ANY'] * 4 / c['SQ_WAVE_CYCLES']:.4f}   "
-        "(4 x SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)" if "SQ_WAIT_INST_ANY" in c else "",
+        f"wave_wait_inst_any         {c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.4f}   "
+        "(SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, both in quad-cycles: share of the waves' life waiting to issue)"
+        if "SQ_WAIT_INST_ANY" in c else "",
+        f"wave_wait_any              {c['SQ_WAIT_ANY'] / c['SQ_WAVE_CYCLES']:.4f}   "
+        "(SQ_WAIT_ANY / SQ_WAVE_CYCLES: share of the waves' life in s_waitcnt)" if "SQ_WAIT_ANY" in c else "",
     ]
     if waves:
         lines += [f"valu_insts_per_wave        {c['SQ_INSTS_VALU'] / waves:.1f}",

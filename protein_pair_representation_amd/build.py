@@ -31,10 +31,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: cannot build libtriattn.so")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the kernels and the C ABI into LIB_PATH (always recompiles)."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
+def build(verbose: bool = False, out: str = LIB_PATH, extra_flags=()) -> str:
+    """Compile the kernels and the C ABI into `out` (always recompiles); extra_flags
+    are added to the hipcc line (e.g. host-only instrumentation for a test build)."""
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-shared", "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,8 +45,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -62,10 +62,13 @@ def header_functions() -> list:
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
+    """The library at `path`, or the in-tree build (TRIATTN_LIB overrides it, e.g. with
+    the sanitizer build of the host code); loaded once."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    path = path or LIB_PATH
+    default = os.environ.get("TRIATTN_LIB") or LIB_PATH
+    path = path or default
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it first (python -m protein_pair_representation_amd.build)")
     lib = ctypes.CDLL(path)
@@ -98,7 +101,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
         fn.argtypes, fn.restype = args, res
-    if path == LIB_PATH:
+    if path == default:
         _lib = lib
     return lib
 
