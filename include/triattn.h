@@ -115,8 +115,10 @@ typedef struct ta_weights {
  *                            log2(e), in tiles of 32 queries x 64 keys (2048
  *                            elements; tile (h, j/32, k/64) at
  *                            ((h*P/32 + j/32)*P/64 + k/64)*2048); inside a tile,
- *                            with k%64 = 16g + 8hh + t, element (j, k) is at
- *                            g*512 + (j%32 + 32*hh)*8 + t.  Keys >= I hold
+ *                            with k%64 = 32st + 16hh + i, element (j, k) is at
+ *                            (st*64 + j%32 + 32*hh)*16 + i (the order of the
+ *                            attention kernel's score accumulators: every lane
+ *                            reads one run of 16).  Keys >= I hold
  *                            -30000 (exp2 of it is 0), query rows >= I filler.
  *                            The end variant holds the transposed bias b_ki at
  *                            (h, i, k); the row block holds the caller's bias.

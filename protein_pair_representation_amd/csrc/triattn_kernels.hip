@@ -58,17 +58,19 @@ constexpr int BUF_DWORD3 = 0x00020000;
 
 __device__ __forceinline__ int rho(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
 
-// Workspace pair-bias layout: fp16 (bf16 problems) or fp32, lane-interleaved tiles.  Tile
-// (h, j/32, k/64) holds the 32 x 64 block a wave adds in one key step as four
-// 16-key chunks; chunk g is exactly the B-operand fragments of that slice
-// (lane j%32 + 32*hh holds keys 16g + 8hh + t, t = 0..7), so each chunk is one
-// contiguous per-lane load: element (j, k) with k%64 = 16g + 8hh + t sits at
-//   g*512 + (j%32 + 32*hh)*8 + t       inside a 2048-element tile.
+// Workspace pair-bias layout: fp16 (bf16 problems) or fp32, tiles in the order of
+// the score accumulators.  Tile (h, j/32, k/64) holds the 32 x 64 block a wave adds
+// in one key step; lane j%32 + 32*hh of a wave holds, for the keys 32*st .. 32*st +
+// 31 of the tile, the scores of its query j and keys 32*st + 16*hh + i (i = 0..15),
+// so its bias is one contiguous run of 16 elements: element (j, k) with k%64 =
+// 32*st + 16*hh + i sits at
+//   (st*64 + j%32 + 32*hh)*16 + i       inside a 2048-element tile,
+// and a wave's 16-element runs of one half tile are 64 consecutive runs.
 // P (a multiple of 128) bounds j, NB (P, or a key block's padded key count) bounds k.
 __device__ __forceinline__ size_t bias_tiled_index(int h, int j, int k, int P, int NB) {
   const int jb = j >> 5, jj = j & 31, kb = k >> 6, kk = k & 63;
-  const int g = kk >> 4, hh = (kk >> 3) & 1, t = kk & 7;
-  return ((((size_t)h * (P >> 5) + jb) * (NB >> 6) + kb) << 11) + (g << 9) + ((jj + 32 * hh) << 3) + t;
+  const int st = kk >> 5, hh = (kk >> 4) & 1, i = kk & 15;
+  return ((((size_t)h * (P >> 5) + jb) * (NB >> 6) + kb) << 11) + (((st << 6) + jj + 32 * hh) << 4) + i;
 }
 
 // ---------------------------------------------------------------- element traits
@@ -99,6 +101,22 @@ __device__ __forceinline__ f32x16 mma(const f32x8& a, const f32x8& b, f32x16 c) 
 #pragma unroll
   for (int t = 0; t < 8; ++t) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], c, 0, 0, 0);
   return c;
+}
+
+// The bias of keys 32*st .. 32*st + 31 of a tile (this lane's run of 16, see
+// bias_tiled_index) as a score accumulator: b[2*st] and b[2*st + 1] are the run's
+// two halves.
+template <typename BF> __device__ __forceinline__ f32x16 bias_acc(const BF (&b)[4], int st) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = (float)b[2 * st + (i >> 3)][i & 7];
+  return r;
+}
+// the four pieces of this lane's bias in a tile (16 B each in fp16, 32 B in fp32)
+template <typename BT, typename BF> __device__ __forceinline__ void load_bias_tile(const BT* btile, int lane,
+                                                                                  BF (&b)[4]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) b[g] = *reinterpret_cast<const BF*>(btile + (((g >> 1) << 6) + lane) * 16 + 8 * (g & 1));
 }
 
 template <typename T> __device__ __forceinline__ typename El<T>::frag to_frag(const float* v);
@@ -842,24 +860,8 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
     for (int s = 0; s < LDT; ++s) kv_lds[buf][l_off[s]] = sreg[s];
   };
 
-  // bias of a key tile as four B-operand fragments (keys 16g + 8hh + t of this
-  // lane's query): one tiled 32 x 64 block (see bias_tiled_index)
-  auto load_bias = [&](const BT* btile, bfrag (&b)[4]) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) b[g] = *reinterpret_cast<const bfrag*>(btile + g * 512 + lane * 8);
-  };
-  // selector A-fragments: row m of the score tile is key rho(m); esel[g] puts a
-  // 1 in contraction slot (hh, t) exactly when rho(m) = 16g + 8hh + t, so that
-  // mma(esel[g], bias chunk) adds each score's own bias
-  bfrag esel[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const int t = rho(lr) - 16 * g - 8 * hh;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = (u == t) ? 1.0f : 0.0f;
-    esel[g] = to_vec8<bfrag>(v);
-  }
+  // bias of a key tile: this lane's runs of one tiled 32 x 64 block (see bias_tiled_index)
+  auto load_bias = [&](const BT* btile, bfrag (&b)[4]) { load_bias_tile<BT, bfrag>(btile, lane, b); };
   const frag e0 = unit_frag<T>(hh == 0 ? 1.0f : 0.0f);  // contraction slot (0,0) = 1
   const f32x16 zero = {};
 
@@ -933,9 +935,9 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       }
     }
 
-    // One key tile for all rows.  The bias scores (two selector products per
-    // 32 keys) are computed once and are the accumulator input of every row's
-    // K Q^T; -m is a last 16-deep slice.  FIRST: the first tile of the head.
+    // One key tile for all rows.  The bias of the tile, converted once, is the
+    // accumulator input of every row's K Q^T; -m is a last 16-deep slice.
+    // FIRST: the first tile of the head.
     auto tile = [&](int kt, auto first_tag) {
       constexpr bool FIRST = decltype(first_tag)::value;
       const int g = h * nbt + kt, buf = g & 1;
@@ -944,9 +946,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       load_tile(hn, kt0 + ktn);                             // stage the next tile
       f32x16 sbias[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) sbias[st] = mma(esel[0], bias_next[2 * st], zero);
-#pragma unroll
-      for (int st = 0; st < 2; ++st) sbias[st] = mma(esel[1], bias_next[2 * st + 1], sbias[st]);
+      for (int st = 0; st < 2; ++st) sbias[st] = bias_acc(bias_next, st);
       load_bias(bias0 + hn * bias_head + ((size_t)(kt0 + ktn) << 11), bias_next);
       // scores of every row first, so that the exponentials of row r run on the
       // VALU while the matrix core still works on row r+1 (and P.V of row r
@@ -1024,9 +1024,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       load_tile(hn, kt0 + ktn);
       f32x16 sbias[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) sbias[st] = mma(esel[0], bias_next[2 * st], zero);
-#pragma unroll
-      for (int st = 0; st < 2; ++st) sbias[st] = mma(esel[1], bias_next[2 * st + 1], sbias[st]);
+      for (int st = 0; st < 2; ++st) sbias[st] = bias_acc(bias_next, st);
       load_bias(bias0 + hn * bias_head + ((size_t)(kt0 + ktn) << 11), bias_next);
       f32x16 sc[ROWS][2];
 #pragma unroll
@@ -1150,9 +1148,8 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
 //  * K/V tiles go through a ring of three LDS slots: tile t + 2 is loaded at the
 //    top of tile t and stored into its slot at the end, so tile t + 1 is already in
 //    LDS while tile t runs (its first scores are computed in tile t's last phase).
-//  * The next tile's bias is loaded at the top of the tile; its selector products
-//    run in the tile's last two phases, once the current scores no longer need
-//    their registers.
+//  * The bias of tile t + 2 is loaded at the top of tile t as well (two tiles of
+//    latency), and each chunk's bias is converted into its score accumulator.
 //  * Row sums come from the matrix core (v_mfma_f32_16x16x32_bf16 with a 0/1
 //    operand, below) instead of 32 dot products per tile on the VALU.
 // Semantics, workgroup grid, redo flags and epilogue are those of tri_attend's
@@ -1251,30 +1248,15 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
   const BT* bias0 = (const BT*)a.bias + ((size_t)(jb < jb_last ? jb : jb_last) * a.bias_kt << 11);
   const size_t bias_head = (size_t)P * a.bias_kt * KT;
   auto load_bias = [&](int h, int kt, bfrag (&b)[4]) {
-    const BT* btile = bias0 + h * bias_head + ((size_t)kt << 11);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) b[g] = *reinterpret_cast<const bfrag*>(btile + g * 512 + lane * 8);
+    load_bias_tile<BT, bfrag>(bias0 + h * bias_head + ((size_t)kt << 11), lane, b);
   };
-  bfrag esel[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const int t = rho(lr) - 16 * g - 8 * hh;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = (u == t) ? 1.0f : 0.0f;
-    esel[g] = to_vec8<bfrag>(v);
-  }
   const frag rsel = rowsum_selector(lane);
   const int rs_src = rowsum_lane(lr);
   const f32x16 zero = {};
-  // selector products: the bias of keys 32 st .. 32 st + 31 of a tile in the score layout
-  auto bias_scores = [&](const bfrag (&b)[4], int st) {
-    return mma(esel[1], b[2 * st + 1], mma(esel[0], b[2 * st], zero));
-  };
 
-  // steps: g = h * nbt + kt walks the key tiles of every head in order; (h1, kt1)
-  // is step g + 1 (its bias is loaded during step g) and (h2, kt2) step g + 2 (its
-  // K/V); past the last step both stay on the last one (loaded, unused)
+  // steps: g = h * nbt + kt walks the key tiles of every head in order; (h2, kt2)
+  // is step g + 2, whose bias and K/V are loaded during step g; past the last step
+  // it stays on the last one (loaded, unused)
   auto advance = [&](int& hx, int& ktx) {
     if (++ktx == nbt) {
       ktx = 0;
@@ -1285,23 +1267,20 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       ktx = nbt - 1;
     }
   };
-  int h1 = 0, kt1 = 0, h2 = 0, kt2 = 0;
+  int h2 = 0, kt2 = 0;
   int slot_cur = 0, slot_nxt = 1, slot_wr = 2;    // ring slots of steps g, g + 1, g + 2
   if (tid == 0) redo_flag = 0;
   bool bad = false;
-  f32x16 sbias[2];
+  bfrag b_cur[4], b_nxt[4];                       // bias of steps g and g + 1
   {
-    bfrag b0[4];
-    load_bias(0, kt0, b0);
+    load_bias(0, kt0, b_cur);
     load_tile(0, kt0);
     store_tile(0);
     advance(h2, kt2);
+    load_bias(h2, kt0 + kt2, b_nxt);
     load_tile(h2, kt0 + kt2);
     store_tile(1);
     advance(h2, kt2);
-    advance(h1, kt1);
-    sbias[0] = bias_scores(b0, 0);
-    sbias[1] = bias_scores(b0, 1);
     __syncthreads();
   }
 
@@ -1330,9 +1309,10 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       o[r] = zero;
       lacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    auto score = [&](int c, const frag (&kf)[2]) {
+    // scores of chunk c: the tile's bias (converted into the accumulator) + K Q^T
+    auto score = [&](int c, const frag (&kf)[2], const bfrag (&b)[4]) {
       const int r = c >> 1;
-      return mma(kf[1], qf[r][1], mma(kf[0], qf[r][0], sbias[c & 1]));
+      return mma(kf[1], qf[r][1], mma(kf[0], qf[r][0], bias_acc(b, c & 1)));
     };
     auto pv = [&](int c, const frag (&vf)[2], const frag (&pf)[2]) {
       const int r = c >> 1;
@@ -1349,8 +1329,8 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
     auto tile = [&](auto first_tag, auto last_tag) {
       constexpr bool FIRST = decltype(first_tag)::value;   // first key tile of the head
       constexpr bool LAST = decltype(last_tag)::value;     // last key tile of the head
-      bfrag bias_nx[4];
-      load_bias(h1, kt0 + kt1, bias_nx);
+      bfrag b_far[4];                              // bias of step g + 2
+      load_bias(h2, kt0 + kt2, b_far);
       load_tile(h2, kt0 + kt2);
       TA_FENCE();
       const u32x4* cur = kv_lds + slot_cur * STAGE_UNITS;
@@ -1374,13 +1354,13 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       frag kfa[2], kfb[2], vfa[2], vfb[2], pf0[2], pf1[2], pf2[2];
       if constexpr (FIRST) {                       // fill: the scores of chunk 0
         kfr(cur, 0, kfa);
-        s_first = score(0, kfa);
+        s_first = score(0, kfa, b_cur);
         TA_FENCE();
       }
       // phase 0: scores of chunk 1, P.V of the previous tile's chunk 3 | exponentials of chunk 0
       kfr(cur, 1, kfa);
       vfr(cur, 0, vfa);
-      const f32x16 s1 = score(1, kfa);
+      const f32x16 s1 = score(1, kfa, b_cur);
       if constexpr (!FIRST) pv(3, vf_last, pf_last);
       expo(0, s_first, pf0);
       TA_SGB(0x100, 4);
@@ -1390,36 +1370,32 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       // phase 1: scores of chunk 2, P.V of chunk 0 | exponentials of chunk 1
       kfr(cur, 2, kfb);
       vfr(cur, 1, vfb);
-      const f32x16 s2 = score(2, kfb);
+      const f32x16 s2 = score(2, kfb, b_cur);
       pv(0, vfa, pf0);
       expo(1, s1, pf1);
       TA_SGB(0x100, 4);
 #pragma unroll
       for (int i = 0; i < 6; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 4); }
       TA_FENCE();
-      // phase 2: scores of chunk 3, P.V of chunk 1, bias products of the next
-      // tile's first half | exponentials of chunk 2
+      // phase 2: scores of chunk 3, P.V of chunk 1 | exponentials of chunk 2
       kfr(cur, 3, kfa);
       vfr(cur, 2, vfa);
-      const f32x16 s3 = score(3, kfa);
+      const f32x16 s3 = score(3, kfa, b_cur);
       pv(1, vfb, pf1);
-      sbias[0] = bias_scores(bias_nx, 0);
       expo(2, s2, pf2);
       TA_SGB(0x100, 4);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 3); }
+      for (int i = 0; i < 6; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 6); }
       TA_FENCE();
-      // phase 3: scores of the next tile's chunk 0, P.V of chunk 2, bias products of
-      // the next tile's second half | exponentials of chunk 3
+      // phase 3: scores of the next tile's chunk 0, P.V of chunk 2 | exponentials of chunk 3
       if constexpr (!LAST) kfr(nxt, 0, kfb);
       vfr(cur, 3, vf_last);
-      if constexpr (!LAST) s_first = score(0, kfb);
+      if constexpr (!LAST) s_first = score(0, kfb, b_nxt);
       pv(2, vfa, pf2);
-      sbias[1] = bias_scores(bias_nx, 1);
       expo(3, s3, pf_last);
       TA_SGB(0x100, LAST ? 2 : 4);
 #pragma unroll
-      for (int i = 0; i < (LAST ? 6 : 8); ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 3); }
+      for (int i = 0; i < (LAST ? 4 : 6); ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, LAST ? 6 : 6); }
       TA_FENCE();
       if constexpr (LAST) pv(3, vf_last, pf_last);  // drain: the head's last chunk
       if constexpr (FIRST) {
@@ -1431,7 +1407,11 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       }
       store_tile(slot_wr);                          // K/V of step g + 2
       __syncthreads();
-      advance(h1, kt1);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        b_cur[g] = b_nxt[g];
+        b_nxt[g] = b_far[g];
+      }
       advance(h2, kt2);
       const int s0 = slot_cur;
       slot_cur = slot_nxt;

@@ -279,8 +279,8 @@ def test_stream_argument():
 
 def untile_bias(raw, P):
     """[H][P][P] from the workspace's tiled bias layout (documented in include/triattn.h)."""
-    t = raw.reshape(4, P // 32, P // 64, 4, 2, 32, 8)        # h, jb, kb, g, hh, jj, t
-    t = t.transpose(0, 1, 5, 2, 3, 4, 6)                      # h, jb, jj, kb, g, hh, t
+    t = raw.reshape(4, P // 32, P // 64, 2, 2, 32, 16)       # h, jb, kb, st, hh, jj, i
+    t = t.transpose(0, 1, 5, 2, 3, 4, 6)                      # h, jb, jj, kb, st, hh, i
     return t.reshape(4, P, P)
 
 
