@@ -30,7 +30,10 @@ struct ProjectArgs {
 struct AttendArgs {
   const void *q, *k, *vt, *g;
   void* o;                // workspace: gated, normalised head outputs, same layout as q
-  const void* bias;       // tiled workspace layout (bias_tiled_index), compute dtype, base-2 units, keys >= I -30000
+  // packed bias (tri_pack_bias, bias_tiled_index: 32-query x 64-key tiles in the
+  // order of the score accumulators), base-2 units, shifted per query row, keys
+  // >= I at -30000; fp16 for bf16 problems, fp32 for fp32 problems
+  const void* bias;
   const void* w_o;
   const float* b_o;       // or nullptr
   void* out;
@@ -63,9 +66,9 @@ hipError_t launch_project(const ProjectArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& a, int dtype, hipStream_t stream);
 // number of int32 flags launch_attend needs in AttendArgs::redo for `lines` lines of I keys
 size_t attend_redo_flags(int lines, int I);
-// tiled dst(h, j, k) = max((src[h][j][k] - max_k src[h][j][k]) * log2(e), -30000) in the
-// compute dtype for Q query rows of K keys (src row stride K); keys >= K -30000, query
-// rows >= Q zero.  dst holds P query positions by NB key positions (NB a multiple of 64).
+// tiled dst(h, j, k) = max((src[h][j][k] - max_k src[h][j][k]) * log2(e), -30000), fp16
+// for bf16 problems (dtype 1) and fp32 for fp32 problems, for Q query rows of K keys
+// (src row stride K); keys >= K -30000, query rows >= Q zero.  dst holds P query positions by NB key positions (NB a multiple of 64).
 // shift (or nullptr) receives max_k src[h][j][k] * log2(e), [H][P] (0 past Q).
 hipError_t launch_pack_bias(const float* src, void* dst, int Q, int K, int P, int NB, float* shift, int dtype,
                             hipStream_t stream);

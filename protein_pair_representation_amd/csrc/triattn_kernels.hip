@@ -783,8 +783,9 @@ __device__ __forceinline__ void out_projection(const AttendArgs& a, int line0, i
 // its gated head outputs in o).  The shifted form (lazy m as described above)
 // then runs only the flagged workgroups of the same grid when a.redo is given,
 // and every workgroup otherwise (key-block calls).  The two forms are separate
-// kernels so that the unshifted one is compiled on its own, with the registers
-// for three waves per SIMD.
+// kernels so that each is compiled with only its own registers.  For bf16 the
+// unshifted form is tri_attend_fast (below); this template's unshifted form
+// serves fp32.
 template <typename T, int ROWS, int WAVES, int MIN_WAVES_PER_SIMD, bool UNSHIFTED>
 __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(AttendArgs a) {
   typedef typename El<T>::frag frag;
@@ -1330,8 +1331,11 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       constexpr bool FIRST = decltype(first_tag)::value;   // first key tile of the head
       constexpr bool LAST = decltype(last_tag)::value;     // last key tile of the head
       bfrag b_far[4];                              // bias of step g + 2
-      load_bias(h2, kt0 + kt2, b_far);
+      // K/V first: the wait for them at the end of the tile then leaves these
+      // bias loads in flight (first used in the last phase of the next tile)
       load_tile(h2, kt0 + kt2);
+      TA_FENCE();
+      load_bias(h2, kt0 + kt2, b_far);
       TA_FENCE();
       const u32x4* cur = kv_lds + slot_cur * STAGE_UNITS;
       const u32x4* nxt = kv_lds + slot_nxt * STAGE_UNITS;
@@ -1406,7 +1410,11 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
         }
       }
       store_tile(slot_wr);                          // K/V of step g + 2
-      __syncthreads();
+      // LDS-only fence: __syncthreads() would also wait for every global load in
+      // flight (vmcnt(0)), the bias of step g + 2 included
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         b_cur[g] = b_nxt[g];
@@ -1423,7 +1431,16 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       tile(std::true_type{}, std::true_type{});
     } else {
       tile(std::true_type{}, std::false_type{});
-      for (int kt = 1; kt < nbt - 1; ++kt) tile(std::false_type{}, std::false_type{});
+      // three tiles per round: the three bias sets and the carried fragments then
+      // rotate by register naming instead of 48 VGPR moves per tile (the compiler
+      // does not unroll a loop with a barrier and a runtime trip count itself)
+      int kt = 1;
+      for (; kt + 3 <= nbt - 1; kt += 3) {
+        tile(std::false_type{}, std::false_type{});
+        tile(std::false_type{}, std::false_type{});
+        tile(std::false_type{}, std::false_type{});
+      }
+      for (; kt < nbt - 1; ++kt) tile(std::false_type{}, std::false_type{});
       tile(std::false_type{}, std::true_type{});
     }
 
@@ -1460,7 +1477,7 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
 // query positions by NB key positions.  Each query row is shifted by its own
 // maximum before the base-2 scale and the rounding: the softmax over keys does not
 // change under a per-query shift, and after it the entries that carry the weight
-// sit near 0, where the rounding error of the compute dtype is smallest; the shift
+// sit near 0, where the absolute rounding error of fp16 (or fp32) is smallest; the shift
 // (base 2) goes to `shift` when the caller needs it (key blocks).  Keys >= K get
 // MASKED; values below MASKED (e.g. -inf, a masked key) are raised to it; padded
 // query rows Q..(Q rounded up to 32)-1 get 0 and a zero shift.
@@ -1585,9 +1602,6 @@ hipError_t launch_pack_bias(const float* src, void* dst, int Q, int K, int P, in
 #ifndef TRIATTN_MINW
 #define TRIATTN_MINW 2  // waves per SIMD the bf16 attention kernel (shifted form) is compiled for
 #endif
-#ifndef TRIATTN_MINW_UNSHIFTED
-#define TRIATTN_MINW_UNSHIFTED 3  // and its unshifted form
-#endif
 #ifndef TRIATTN_WAVES
 #define TRIATTN_WAVES 4
 #endif
@@ -1609,8 +1623,8 @@ hipError_t launch_attend(const AttendArgs& args, int dtype, hipStream_t stream) 
   const bool one_pass = !a.state_in && !a.state_out && a.redo != nullptr && a.nbt > 0;
   if (!one_pass) a.redo = nullptr;
   const dim3 g((unsigned)nblk), b(W * 64);
-  // bf16: the unshifted form at three waves per SIMD, the shifted form at two;
-  // fp32 (twice the fragment registers): one
+  // bf16: the one-pass kernel and the shifted form at two waves per SIMD; fp32
+  // (twice the fragment registers): one
   if (dtype == 1) {
     if (one_pass) hipLaunchKernelGGL((tri_attend_fast<TRIATTN_MINW_FAST>), g, b, 0, stream, a);
     hipLaunchKernelGGL((tri_attend<__bf16, R, W, TRIATTN_MINW, false>), g, b, 0, stream, a);
