@@ -432,8 +432,23 @@ SQ_PASSES = [
 ]
 
 
-def summarize_sq(run_dir, workload):
-    """Write the attention kernel's SQ counter summary (matrix-core and VALU activity).
+def _sq_target(workload, family):
+    """(kernel short name, bench command, summary path, source hash) of an SQ summary."""
+    if family == "knn":
+        return ("knn_select_encode", "python3 $R/bench.py --knn-only --steps 3",
+                os.path.join(PROFILE_DIR, "knn_select_encode_knn-L16384-k32_sq.txt"), kernel_sha(KNN_SRC))
+    if family == "aaq":
+        return ("aaq_encode_A_bf16", f"python3 $R/bench.py --workload {workload} --aaq-only --steps 3",
+                os.path.join(PROFILE_DIR, f"aaq_encode_A_bf16_{workload}_sq.txt"), kernel_sha(AAQ_SRC))
+    return ("tri_attend", f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline "
+            "--key-blocks 0 --aaq 0 --knn 0 --other-workloads 0",
+            os.path.join(PROFILE_DIR, f"tri_attend_{workload}_sq.txt"), kernel_sha())
+
+
+def summarize_sq(run_dir, workload, family="tri"):
+    """Write a kernel's SQ counter summary (matrix-core and VALU activity): the
+    one-pass attention kernel, or with family "knn" / "aaq" the kNN selection or
+    the group-A encode kernel.
 
     run_dir holds sq1/ sq2/ sq3/: bench.py under the three counter sets of SQ_PASSES.
     rocprofv3 reports each counter summed over the device; GRBM_GUI_ACTIVE is summed
@@ -444,6 +459,7 @@ def summarize_sq(run_dir, workload):
     import collections
     import csv
     import glob
+    kname, cmd, path, sha = _sq_target(workload, family)
     acc = collections.defaultdict(list)
     durations = []
     for n in range(1, len(SQ_PASSES) + 1):
@@ -452,7 +468,7 @@ def summarize_sq(run_dir, workload):
             raise SystemExit(f"expected one counter_collection.csv under {run_dir}/sq{n}")
         per = collections.defaultdict(dict)
         for r in csv.DictReader(open(files[0])):
-            if _short(r["Kernel_Name"]) != "tri_attend":
+            if _short(r["Kernel_Name"]) != kname:
                 continue
             per[r["Dispatch_Id"]][r["Counter_Name"]] = float(r["Counter_Value"])
             if n == 1 and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
@@ -471,14 +487,16 @@ def summarize_sq(run_dir, workload):
 
     mfma, valu, coex = frac("SQ_VALU_MFMA_BUSY_CYCLES"), frac("SQ_ACTIVE_INST_VALU", True), \
         frac("SQ_VALU_MFMA_COEXEC_CYCLES")
-    lines = [f"# SQ counters of the one-pass attention kernel (tri_attend), workload {workload}, gfx950 (MI355X)",
+    what = "the one-pass attention kernel (tri_attend)" if family == "tri" else kname
+    if family == "knn":
+        workload = "knn-L16384-k32"
+    lines = [f"# SQ counters of {what}, workload {workload}, gfx950 (MI355X)",
              "# commands (R = repository root, O = output directory, run from /tmp), n = 1, 2, 3 over the counter sets:"]
     for n, pset in enumerate(SQ_PASSES, 1):
-        lines.append(f"#   timeout -s KILL 100 rocprofv3 --pmc {pset} --output-format csv -d $O/sq{n} -o s -- "
-                     f"python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline "
-                     "--key-blocks 0 --aaq 0 --knn 0 --other-workloads 0")
-    lines.append(f"#   python3 bench.py --summarize-sq $O --workload {workload}")
-    lines.append(f"# kernel_sha={kernel_sha()}")
+        lines.append(f"#   timeout -s KILL 100 rocprofv3 --pmc {pset} --output-format csv -d $O/sq{n} -o s -- {cmd}")
+    lines.append(f"#   python3 bench.py --summarize-sq $O --workload {workload}"
+                 + (f" --family {family}" if family != "tri" else ""))
+    lines.append(f"# kernel_sha={sha}")
     lines.append("# normalisation: per SIMD, counter / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs);"
                  " SQ_ACTIVE_INST_* are in quad-cycles (x 4), SQ_WAVE_CYCLES and SQ_WAIT_* in quad-cycles too")
     lines += [f"{k:28s} {v:18.1f}" for k, v in sorted(c.items())]
@@ -504,7 +522,6 @@ def summarize_sq(run_dir, workload):
                   f"lds_insts_per_wave         {c['SQ_INSTS_LDS'] / waves:.1f}",
                   f"salu_insts_per_wave        {c['SQ_INSTS_SALU'] / waves:.1f}",
                   f"vmem_insts_per_wave        {c['SQ_INSTS_VMEM'] / waves:.1f}"]
-    path = os.path.join(PROFILE_DIR, f"tri_attend_{workload}_sq.txt")
     open(path, "w").write("\n".join(x for x in lines if x) + "\n")
     print("\n".join(lines))
 
@@ -575,7 +592,7 @@ def main():
                     help="write the attention kernel's SQ counter summary under profiles/ from rocprofv3 --pmc runs "
                          "in DIR, and exit")
     ap.add_argument("--family", default="tri", choices=["tri", "aaq", "knn"],
-                    help="kernel family of --summarize-pmc / --summarize-trace")
+                    help="kernel family of --summarize-pmc / --summarize-trace / --summarize-sq")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.workload, args.copy_mib, args.family)
@@ -584,7 +601,7 @@ def main():
         summarize_trace(args.summarize_trace, args.workload, args.steps, args.warmup, args.family)
         return
     if args.summarize_sq:
-        summarize_sq(args.summarize_sq, args.workload)
+        summarize_sq(args.summarize_sq, args.workload, args.family)
         return
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
