@@ -276,7 +276,9 @@ def key_blocks(ws, wd, I, R, dt, variant, nb, stream, k2_flops, k2_ms, reps=10):
 
 def kv_blocks(ws, wd, I, R, dt, variant, nb, stream, k2_flops, k2_ms, reps=10):
     """The ring step: NB caller-held key blocks (copies of the workspace's keys, values and
-    bias columns, padded to 64 positions) folded into a carried state, then finalize."""
+    bias columns, padded to 64 positions) folded into a carried state, the last one
+    folded and finished in one launch (and, for comparison, every block folded, then
+    a separate finalize)."""
     import torch
     from protein_pair_representation_amd import triattn as ta
     v = ta.workspace_views(ws, I, R, dt, variant)
@@ -293,24 +295,34 @@ def kv_blocks(ws, wd, I, R, dt, variant, nb, stream, k2_flops, k2_ms, reps=10):
     st = ta.state(I, R, dt, variant)
     out = torch.empty((R, I, 128), dtype=dt, device="cuda")
 
-    def once():
+    def ring(fused_last):
         for n, (kb, vb, bb, nk) in enumerate(blocks):
-            ta.triangle_attn_attend_kv_block(ws, wd, I, R, dt, kb, vb, bb, nk, n == 0, st, variant=variant,
-                                             stream=stream)
-        ta.triangle_attn_attend_finalize(ws, wd, I, R, dt, st, variant=variant, out=out, stream=stream)
+            if fused_last and n == len(blocks) - 1:
+                ta.triangle_attn_attend_kv_block_final(ws, wd, I, R, dt, kb, vb, bb, nk, n == 0, st,
+                                                       variant=variant, out=out, stream=stream)
+            else:
+                ta.triangle_attn_attend_kv_block(ws, wd, I, R, dt, kb, vb, bb, nk, n == 0, st, variant=variant,
+                                                 stream=stream)
+        if not fused_last:
+            ta.triangle_attn_attend_finalize(ws, wd, I, R, dt, st, variant=variant, out=out, stream=stream)
 
-    once()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        once()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    def timed(fused_last):
+        ring(fused_last)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            ring(fused_last)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_sep = timed(False)
+    ms = timed(True)
     return {"variant": variant, "blocks": len(blocks), "block_keys": size, "ms": round(ms, 4),
             "TFLOP/s": round(k2_flops / (ms * 1e-3) / 1e12, 2), "one_pass_ms": round(k2_ms, 4),
-            "time_vs_one_pass": round(ms / k2_ms, 3)}
+            "time_vs_one_pass": round(ms / k2_ms, 3), "last_block": "folded and finished in one launch",
+            "ms_with_separate_finalize": round(ms_sep, 4)}
 
 
 def _limit_blas():

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TRIATTN_ABI_VERSION 5
+#define TRIATTN_ABI_VERSION 6
 
 /* Compute dtypes. */
 enum { TA_BF16 = 1, TA_F32 = 2 };
@@ -219,7 +219,8 @@ int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* 
  *           workspace by this call (bias required).  Zero: the state carries the
  *           earlier blocks, bias is ignored (may be NULL)
  *   state   fp32, triangle_attn_state_bytes() bytes: O [L][H][P][d], then at the
- *           next 256-byte boundary (m, l) [L][H][P][2] (L, P as in the layout)
+ *           next 256-byte boundary (m, l) [L][H][P][2] (L, P as in the layout),
+ *           then at the next one [H][P] of scratch for caller-held blocks
  *   ws      filled by triangle_attn_project with the same problem and variant */
 int triangle_attn_state_bytes(const ta_problem* prob, int variant, size_t* bytes);
 int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_weights* w,
@@ -253,7 +254,7 @@ int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_wei
  *                triangle_attn_attend_block, whose m is relative to the whole
  *                row's bias maximum, are not to be mixed with these)
  *   state, ws    as for triangle_attn_attend_block; this call overwrites the
- *                workspace's packed-bias and o regions (scratch between calls)
+ *                workspace's packed-bias region (scratch between calls)
  * Errors: TA_ERR_NULL_PTR, TA_ERR_MISALIGNED, TA_ERR_BAD_SHAPE (nkeys or
  * kv_positions out of range), TA_ERR_ALIAS (state or ws overlapping a block or
  * each other), TA_ERR_WORKSPACE_TOO_SMALL; nothing is enqueued on error. */
@@ -261,6 +262,23 @@ int triangle_attn_attend_kv_block(const ta_problem* prob, int variant, const ta_
                                   const void* k_blk, const void* vt_blk, int32_t kv_positions,
                                   const float* bias_blk, int32_t nkeys, int32_t first,
                                   float* state, void* ws, size_t ws_bytes, void* stream);
+
+/* The last step of a ring: folds the last caller-held block into the carried
+ * state and finishes the rows (o = O / l, gate, output projection) into `out`,
+ * in one launch: what triangle_attn_attend_kv_block followed by
+ * triangle_attn_attend_finalize computes, without writing the fp32 state and
+ * reading it back.  The state is read (unless `first`, which makes this block
+ * the only one) and is not updated, except for its scratch tail.  Arguments as
+ * for triangle_attn_attend_kv_block, plus out as in triangle_attn_attend (rows x
+ * I x c_z in the compute dtype, or transposed for TA_END); it also writes the
+ * workspace's o region.
+ * Errors: those of triangle_attn_attend_kv_block; TA_ERR_NULL_PTR for a NULL out,
+ * TA_ERR_ALIAS for out overlapping a block, the state, the workspace or a weight. */
+int triangle_attn_attend_kv_block_final(const ta_problem* prob, int variant, const ta_weights* w,
+                                        const void* k_blk, const void* vt_blk, int32_t kv_positions,
+                                        const float* bias_blk, int32_t nkeys, int32_t first,
+                                        float* state, void* out, void* ws, size_t ws_bytes,
+                                        void* stream);
 
 /* triangle_attn_start without a workspace argument and without any allocation,
  * for callers that cannot allocate device memory (code under HIP graph capture,

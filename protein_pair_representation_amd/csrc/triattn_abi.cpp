@@ -161,10 +161,14 @@ triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weigh
   return a;
 }
 
-// State of the key-block stage: O [L][H][P][d] fp32, then (m, l) [L][H][P][2] fp32.
-void state_sizes(const ta_ws_layout& l, size_t* o_bytes, size_t* total) {
+// State of the key-block stage: O [L][H][P][d] fp32, then (m, l) [L][H][P][2] fp32,
+// then the per-(head, query) shift [H][P] fp32 of the last caller-held block's
+// packed bias (written by that call's pack, read by its attention launch).
+void state_sizes(const ta_ws_layout& l, size_t* o_bytes, size_t* total, size_t* shift_off = nullptr) {
   *o_bytes = align256((size_t)l.lines * kHeads * l.positions * kHeadDim * sizeof(float));
-  *total = *o_bytes + align256((size_t)l.lines * kHeads * l.positions * 2 * sizeof(float));
+  const size_t sh = *o_bytes + align256((size_t)l.lines * kHeads * l.positions * 2 * sizeof(float));
+  if (shift_off) *shift_off = sh;
+  *total = sh + align256((size_t)kHeads * l.positions * sizeof(float));
 }
 
 int enqueue(hipError_t e) { return e == hipSuccess ? TA_OK : TA_ERR_HIP; }
@@ -424,15 +428,23 @@ int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_wei
   return enqueue(triattn::launch_attend(a, prob->dtype, (hipStream_t)stream));
 }
 
-int triangle_attn_attend_kv_block(const ta_problem* prob, int variant, const ta_weights* w, const void* k_blk,
-                                  const void* vt_blk, int32_t kv_positions, const float* bias_blk, int32_t nkeys,
-                                  int32_t first, float* state, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One caller-held key block: pack its bias (shift into the state's tail), then the
+// shifted attention form folds it into the state (out == nullptr) or, for the last
+// block, folds it and finishes the rows into out without writing the state.
+int kv_block(const ta_problem* prob, int variant, const ta_weights* w, const void* k_blk, const void* vt_blk,
+             int32_t kv_positions, const float* bias_blk, int32_t nkeys, int32_t first, float* state, void* out,
+             void* ws, size_t ws_bytes, void* stream) {
   int rc = check_problem(prob, variant);
   if (rc) return rc;
   if ((rc = check_weights(w))) return rc;
   if (k_blk == nullptr || vt_blk == nullptr || bias_blk == nullptr || state == nullptr || ws == nullptr)
     return TA_ERR_NULL_PTR;
-  if (!aligned16(k_blk) || !aligned16(vt_blk) || !aligned16(bias_blk) || !aligned16(state) || !aligned16(ws))
+  if (!aligned16(k_blk) || !aligned16(vt_blk) || !aligned16(bias_blk) || !aligned16(state) || !aligned16(ws) ||
+      (out != nullptr && !aligned16(out)))
     return TA_ERR_MISALIGNED;
   ta_ws_layout l;
   layout_of(prob, variant, &l);
@@ -442,25 +454,27 @@ int triangle_attn_attend_kv_block(const ta_problem* prob, int variant, const ta_
       kv_positions > l.positions)
     return TA_ERR_BAD_SHAPE;
   if (ws_bytes < l.total) return TA_ERR_WORKSPACE_TOO_SMALL;
-  size_t ob, sb;
-  state_sizes(l, &ob, &sb);
+  size_t ob, sb, shift_off;
+  state_sizes(l, &ob, &sb, &shift_off);
   const size_t es = esize(prob->dtype);
   const size_t kv_bytes = (size_t)l.lines * kHeads * kv_positions * kHeadDim * es;
   const Span kspan = {k_blk, kv_bytes}, vspan = {vt_blk, kv_bytes};
   const Span bspan = {bias_blk, (size_t)kHeads * prob->I * nkeys * sizeof(float)};
   const Span wspan = {ws, l.total}, sspan = {state, sb};
-  // state and workspace are written: neither may overlap anything else
+  const Span ospan = {out, out ? (size_t)prob->rows * prob->I * kCz * es : 0};
+  // state, workspace and out are written: none may overlap anything else
   const Span ins[] = {kspan, vspan, bspan};
   for (const Span& x : ins)
-    if (overlap(x, wspan) || overlap(x, sspan)) return TA_ERR_ALIAS;
-  if ((rc = check_out_alias(prob, w, sspan, {nullptr, 0}, wspan, {nullptr, 0}))) return rc;
+    if (overlap(x, wspan) || overlap(x, sspan) || overlap(x, ospan)) return TA_ERR_ALIAS;
+  if ((rc = check_out_alias(prob, w, sspan, {nullptr, 0}, wspan, ospan))) return rc;
+  if (out != nullptr && (rc = check_out_alias(prob, w, ospan, {nullptr, 0}, wspan, sspan))) return rc;
   (void)hipGetLastError();
   char* base = (char*)ws;
-  float* shift = (float*)(base + l.o);  // the o region is free during key-block calls
+  float* shift = (float*)((char*)state + shift_off);
   if ((rc = enqueue(triattn::launch_pack_bias(bias_blk, base + l.bias, prob->I, nkeys, l.positions, kv_positions,
                                               shift, prob->dtype, (hipStream_t)stream))))
     return rc;
-  triattn::AttendArgs a = attend_args(prob, variant, w, nullptr, nullptr, ws, l);
+  triattn::AttendArgs a = attend_args(prob, variant, w, nullptr, out, ws, l);
   a.k = k_blk;
   a.vt = vt_blk;
   a.kv_P = kv_positions;
@@ -468,11 +482,32 @@ int triangle_attn_attend_kv_block(const ta_problem* prob, int variant, const ta_
   a.bias_shift = shift;
   a.kt0 = 0;
   a.nbt = (nkeys + kKeyTile - 1) / kKeyTile;
+  a.redo = nullptr;  // the shifted form only: it reads k / v^T at kv_positions
   a.state_o = state;
   a.state_ml = (float*)((char*)state + ob);
   a.state_in = first ? 0 : 1;
-  a.state_out = 1;
+  a.state_out = out == nullptr ? 1 : 0;
   return enqueue(triattn::launch_attend(a, prob->dtype, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int triangle_attn_attend_kv_block(const ta_problem* prob, int variant, const ta_weights* w, const void* k_blk,
+                                  const void* vt_blk, int32_t kv_positions, const float* bias_blk, int32_t nkeys,
+                                  int32_t first, float* state, void* ws, size_t ws_bytes, void* stream) {
+  return kv_block(prob, variant, w, k_blk, vt_blk, kv_positions, bias_blk, nkeys, first, state, nullptr, ws,
+                  ws_bytes, stream);
+}
+
+int triangle_attn_attend_kv_block_final(const ta_problem* prob, int variant, const ta_weights* w,
+                                        const void* k_blk, const void* vt_blk, int32_t kv_positions,
+                                        const float* bias_blk, int32_t nkeys, int32_t first, float* state,
+                                        void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (out == nullptr) return TA_ERR_NULL_PTR;
+  return kv_block(prob, variant, w, k_blk, vt_blk, kv_positions, bias_blk, nkeys, first, state, out, ws,
+                  ws_bytes, stream);
 }
 
 int triangle_attn_attend_finalize(const ta_problem* prob, int variant, const ta_weights* w, const float* state,

@@ -91,6 +91,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "triangle_attn_attend_finalize": ([P, i32, W, vp, vp, vp, sz, vp], i32),
         "triangle_attn_attend_kv_block": ([P, i32, W, vp, vp, ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32,
                                            vp, vp, sz, vp], i32),
+        "triangle_attn_attend_kv_block_final": ([P, i32, W, vp, vp, ctypes.c_int32, vp, ctypes.c_int32,
+                                                 ctypes.c_int32, vp, vp, vp, sz, vp], i32),
         "triangle_attn_project_aaq": ([P, i32, W, vp, i32, vp, sz, vp], i32),
         "aaq_record_bytes": ([i32], i32),
         "aaq_encode": ([vp, i32, ctypes.c_int64, i32, vp, vp], i32),
@@ -310,6 +312,23 @@ def triangle_attn_attend_kv_block(ws, weights, I, rows, dtype, k_blk, vt_blk, bi
         _ptr(k_blk), _ptr(vt_blk), int(nb), _ptr(bias_blk), int(nkeys), int(bool(first)), _ptr(st), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
     return st
+
+
+def triangle_attn_attend_kv_block_final(ws, weights, I, rows, dtype, k_blk, vt_blk, bias_blk, nkeys, first, st,
+                                        variant="start", out=None, stream=None, eps=1e-5):
+    """Fold the last caller-held key block and finish the rows into `out` (see include/triattn.h)."""
+    _dev(ws, "ws")
+    _dev(st, "state", torch.float32)
+    _dev(k_blk, "k_blk", dtype)
+    _dev(vt_blk, "vt_blk", dtype)
+    _dev(bias_blk, "bias_blk", torch.float32)
+    out = torch.empty((rows, I, C_Z), dtype=dtype, device=ws.device) if out is None else _dev(out, "out", dtype)
+    nb = k_blk.shape[2]
+    _check(load_library().triangle_attn_attend_kv_block_final(
+        ctypes.byref(problem(I, rows, dtype, eps)), VARIANTS[variant], ctypes.byref(weights_struct(weights, dtype)),
+        _ptr(k_blk), _ptr(vt_blk), int(nb), _ptr(bias_blk), int(nkeys), int(bool(first)), _ptr(st), _ptr(out),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
 
 
 def triangle_attn_attend_finalize(ws, weights, I, rows, dtype, st, variant="start", out=None, stream=None,

@@ -40,13 +40,13 @@ def layout(lib, p, variant):
 
 def test_exports_match_header(lib):
     names = ta.header_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror(lib):
-    assert lib.triangle_attn_abi_version() == 5
+    assert lib.triangle_attn_abi_version() == 6
     for code in range(0, -13, -1):
         msg = lib.triangle_attn_strerror(code).decode()
         assert msg and msg != "unknown error code"
@@ -184,7 +184,8 @@ def test_state_bytes(lib):
     assert lib.triangle_attn_state_bytes(ctypes.byref(p), ta.TA_START, ctypes.byref(n)) == 0
     P = 1024
     o = (1000 * 4 * P * 32 * 4 + 255) // 256 * 256
-    assert n.value == o + (1000 * 4 * P * 2 * 4 + 255) // 256 * 256
+    ml = (1000 * 4 * P * 2 * 4 + 255) // 256 * 256
+    assert n.value == o + ml + 4 * P * 4                 # + the [H][P] shift scratch of caller-held blocks
     assert lib.triangle_attn_state_bytes(ctypes.byref(p), ta.TA_START, None) == -1
     assert lib.triangle_attn_state_bytes(ctypes.byref(prob(I=64, rows=32)), ta.TA_START, ctypes.byref(n)) == -2
 
@@ -257,6 +258,29 @@ def test_kv_block_rejects(lib):
     assert call(k=WS + 4096) == -7           # key block inside the workspace
     assert call(bias=ST + 256) == -7         # bias block inside the state
     assert call(variant=9) == -9
+
+
+def test_kv_block_final_rejects(lib):
+    """The last ring step: the key-block checks, plus the output buffer."""
+    p = prob(I=200)
+    w = weights()
+    rc, lay = layout(lib, p, ta.TA_START)
+    f = lib.triangle_attn_attend_kv_block_final
+    K, V, B, ST, WS, OUT = A + 400 * MB, A + 450 * MB, A + 500 * MB, A + 300 * MB, A + 200 * MB, A + 600 * MB
+
+    def call(k=K, npos=128, nkeys=100, st=ST, out=OUT, ws=WS):
+        return f(ctypes.byref(p), ta.TA_START, ctypes.byref(w), k, V, npos, B, nkeys, 0, st, out, ws, lay.total,
+                 None)
+
+    assert call() != -2 and call() != -1
+    assert call(out=None) == -1
+    assert call(out=OUT + 8) == -6
+    assert call(nkeys=0) == -2 and call(npos=96) == -2
+    assert call(out=K + 4096) == -7          # out over the key block
+    assert call(out=WS + 4096) == -7         # out inside the workspace
+    assert call(out=ST + 256) == -7          # out inside the state
+    assert call(out=A + 900 * MB) == -7      # out over a weight
+    assert call(k=OUT) == -7                 # key block over out
 
 
 # ----------------------------------------------------------------------------------------- AAQ codec

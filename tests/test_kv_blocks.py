@@ -82,6 +82,58 @@ def test_kv_blocks_match_oracle(variant, I, dtype, sizes, order):
     check(out, inputs.to_f64(one_pass), dtype, "kv blocks vs one pass")
 
 
+@pytest.mark.parametrize("variant,I,dtype,sizes", [("start", 200, "bf16", (70, 64, 66)),
+                                                   ("end", 200, "bf16", (128, 72)),
+                                                   ("start", 130, "f32", (64, 66)),
+                                                   ("end", 65, "f32", (1, 64))])
+@pytest.mark.parametrize("order", ["forward", "shuffled"])
+def test_kv_block_final(variant, I, dtype, sizes, order):
+    """The last block folded and finished in one launch: against the oracle, and
+    against the same blocks folded one by one and finalised separately; the state
+    is left as the previous blocks left it."""
+    say(f"[kv final] {variant} I={I} {dtype} blocks {sizes} {order}")
+    w = weights_with_extras(600 + I, dtype)
+    z = inputs.make_z(600 + I, I, dtype)
+    wd = dev(w)
+    ws = ta.triangle_attn_project(z.cuda(), wd, variant=variant)
+    bias = ta.workspace_views(ws, I, I, TDT[dtype], variant)["bias_f32"].clone()
+    blocks = cut_blocks(ws, I, I, dtype, variant, sizes, bias)
+    seq = ORDERS[order](len(blocks))
+    st = fold(ws, wd, I, I, dtype, variant, blocks, seq)
+    two_step = ta.triangle_attn_attend_finalize(ws, wd, I, I, TDT[dtype], st, variant=variant)
+    st = fold(ws, wd, I, I, dtype, variant, blocks, seq[:-1])
+    st_before = st.clone()
+    kb, vb, bb, nk = blocks[seq[-1]]
+    buf, out = guarded((I, I, 128), TDT[dtype])
+    ta.triangle_attn_attend_kv_block_final(ws, wd, I, I, TDT[dtype], kb, vb, bb, nk, False, st, variant=variant,
+                                           out=out)
+    torch.cuda.synchronize()
+    assert guards_intact(buf), "write outside the output"
+    n_ml = st.numel() - 4 * ((I + 255) // 256 * 256)             # O and (m, l): all but the shift scratch
+    assert torch.equal(st[:n_ml].view(torch.int32), st_before[:n_ml].view(torch.int32)), \
+        "the final call must not update the state"
+    f = ref.triangle_attn_start if variant == "start" else ref.triangle_attn_end
+    check(out, f(inputs.to_f64(z), params64(w)), dtype, f"kv final {variant} I={I}")
+    check(out, inputs.to_f64(two_step), dtype, "kv final vs fold + finalize")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kv_block_final_single_block(dtype):
+    """Every key as one caller-held block, first and last at once: the state is never read."""
+    I = 200
+    say(f"[kv final] one block, I={I} {dtype}")
+    w = weights_with_extras(650, dtype)
+    z = inputs.make_z(650, I, dtype)
+    wd = dev(w)
+    ws = ta.triangle_attn_project(z.cuda(), wd, variant="start")
+    bias = ta.workspace_views(ws, I, I, TDT[dtype], "start")["bias_f32"].clone()
+    (kb, vb, bb, nk), = cut_blocks(ws, I, I, dtype, "start", (I,), bias)
+    st = torch.full_like(ta.state(I, I, TDT[dtype], "start"), float("nan"))   # never read
+    out = ta.triangle_attn_attend_kv_block_final(ws, wd, I, I, TDT[dtype], kb, vb, bb, nk, True, st)
+    torch.cuda.synchronize()
+    check(out, ref.triangle_attn_start(inputs.to_f64(z), params64(w)), dtype, "kv final, one block")
+
+
 @pytest.mark.parametrize("order", [[0, 1, 2], [2, 0, 1]])
 def test_kv_blocks_rows_large_offsets(order):
     """Row block with a caller bias carrying per-query offsets of +-30 and keys
@@ -142,6 +194,14 @@ def test_kv_blocks_workload_1024():
     ta.triangle_attn_attend_finalize(ws, wd, I, I, torch.bfloat16, st, variant="start", out=out)
     torch.cuda.synchronize()
     check(out.cpu(), inputs.to_f64(one_pass), "bf16", "kv blocks vs one pass at I=1024")
+    # the same ring with the last block folded and finished in one launch
+    st = fold(ws, wd, I, I, "bf16", "start", blocks, [3, 1, 0])
+    out_f = torch.full((I, I, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kb, vb, bb, nk = blocks[2]
+    ta.triangle_attn_attend_kv_block_final(ws, wd, I, I, torch.bfloat16, kb, vb, bb, nk, False, st, out=out_f)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out_f).any(), "unwritten outputs"
+    check(out_f.cpu(), inputs.to_f64(out), "bf16", "kv final vs fold + finalize at I=1024")
     p = params64(w)
     z64 = inputs.to_f64(z)
     maxabs, rel, nonfin, n = oracle_pool.compare("start", z64, ref.pair_bias(z64, p), p,
