@@ -696,27 +696,30 @@ __device__ __forceinline__ float rebase_tile(f32x16 (&s)[2], typename El<T>::fra
 }
 
 // Workgroup -> (line group, query block).  Workgroups are dealt to the 8 XCDs
-// round-robin (XCD x runs blocks x, x+8, ...).  Mode 2 splits the XCDs 4 x 2:
-// XCD x serves the query blocks congruent to x % 4 and one half of the line
-// groups, two query blocks at a time, so the bias slice it reads stays resident
-// in its L2 while each line group's keys and values are read by only 4 XCDs,
-// all walking the lines in step (the first read brings them into the last-level
-// cache for the other three).  Mode 0 takes the blocks in order, every query
-// block of a line group side by side.  The launcher picks mode 2 for I < 2048
-// and mode 0 above, where it measured faster (3% at I = 4096); mode 2 falls
-// back to mode 0 when the shape does not divide.
+// round-robin (XCD x runs blocks x, x+8, ...).  Mode 4 pairs the XCDs: XCD x
+// serves the line groups congruent to x >> 1 (mod 4) and, of each, the half of
+// the query blocks given by x & 1, so a line group's keys and values are read by
+// two XCDs only and an XCD's bias slice is half of the bias.  Mode 2 splits the
+// XCDs 4 x 2: XCD x serves the query blocks congruent to x % 4 and one half of
+// the line groups, two query blocks at a time, each line group's keys and values
+// read by 4 XCDs walking the lines in step.  Mode 0 takes the blocks in order,
+// every query block of a line group side by side.  The launcher picks mode 4 up
+// to I = 2048 (1.3% faster than mode 2 at I = 1024 and than mode 0 at I = 2048)
+// and mode 0 above (3% faster than mode 2 at I = 4096); a mode whose shape does
+// not divide falls back to the next (4 -> 2 -> 0).
 __device__ __forceinline__ void map_block(int mode, int bid, int n_lg, int nqb, int& lg, int& qb) {
-  if (mode == 2 && nqb % 8 == 0 && n_lg % 2 == 0) {
+  if (mode == 4 && n_lg % 4 == 0 && nqb % 2 == 0) {
+    const int x = bid & 7, slot = bid >> 3, nh = nqb >> 1;
+    lg = (slot / nh) * 4 + (x >> 1);
+    qb = (x & 1) * nh + slot % nh;
+    return;
+  }
+  if (mode >= 2 && nqb % 8 == 0 && n_lg % 2 == 0) {
     const int x = bid & 7, slot = bid >> 3;
     const int alpha = x & 3, beta = x >> 2, n_half = n_lg >> 1;
     const int phase = slot / (2 * n_half), rem = slot - phase * 2 * n_half;
     lg = beta * n_half + (rem >> 1);
     qb = alpha + 4 * (2 * phase + (rem & 1));
-  } else if (mode == 1 && nqb % 8 == 0) {
-    const int x = bid & 7, slot = bid >> 3;
-    const int phase = slot / n_lg;
-    lg = slot - phase * n_lg;
-    qb = phase * 8 + x;
   } else {
     lg = bid / nqb;
     qb = bid - lg * nqb;
@@ -1618,7 +1621,7 @@ hipError_t launch_attend(const AttendArgs& args, int dtype, hipStream_t stream) 
   constexpr int R = TRIATTN_ROWS, W = TRIATTN_WAVES;
   AttendArgs a = args;
   a.nqb = (a.I + 32 * W - 1) / (32 * W);
-  a.xcd_mode = a.I < 2048 ? 2 : 0;
+  a.xcd_mode = a.I <= 2048 ? 4 : 0;
   const long nblk = (long)((a.lines + R - 1) / R) * a.nqb;
   const bool one_pass = !a.state_in && !a.state_out && a.redo != nullptr && a.nbt > 0;
   if (!one_pass) a.redo = nullptr;
