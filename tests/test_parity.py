@@ -6,7 +6,7 @@ Tolerances (compared element by element on the stored outputs, upcast exactly):
   fp32:                           max |gpu - ref| <= 1e-5
 Small and ragged sizes are compared on every output, and so is the I = 1024
 workload (both variants, over a process pool).  The I = 2048 and the row-block
-I = 4096 workloads are compared on eight whole lines each (every query block),
+I = 4096 workloads are compared on ten and eight whole lines (every query block),
 with every output checked to be written and finite.
 """
 import numpy as np
@@ -371,14 +371,15 @@ def test_workload_i1024_every_token(variant):
 
 
 # lines of the larger workloads compared in full (every query): both lines of
-# some line pairs, first and last lines, and lines from both halves
-LINES_I2048 = [0, 1, 510, 777, 1024, 1025, 2046, 2047]
+# some line pairs, first and last lines, lines from both halves, and at I = 2048
+# line pairs of every residue mod 4 (the XCD pair that serves a line pair)
+LINES_I2048 = [0, 1, 2, 5, 510, 777, 1024, 1025, 2046, 2047]
 LINES_R1024 = [0, 1, 255, 510, 511, 512, 1022, 1023]
 
 
 @pytest.mark.timeout(1500)
 def test_workload_i2048_outliers_lines():
-    """I = 2048 with outlier channels: eight whole lines (every query block) against the oracle."""
+    """I = 2048 with outlier channels: ten whole lines (every query block) against the oracle."""
     name = "start-bf16-I2048-outliers"
     say(f"[workload] {name}: lines {LINES_I2048}, every query")
     wl, w = _workload(name)
