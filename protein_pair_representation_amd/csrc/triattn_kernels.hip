@@ -1300,16 +1300,24 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
     for (int cc = 0; cc < 2; ++cc) vf[cc] = lds_frag<T, VU>(vl, rho(lr), 4 * (c & 1) + 2 * hh + cc);
   };
 
-#pragma unroll 1
-  for (int h = 0; h < NH; ++h) {
-    frag qf[ROWS][2];
-    f32x16 o[ROWS];
-    f32x4 lacc[ROWS];
+  // q of head h: this lane's query on both rows.  Heads after the first are loaded in
+  // the last phase of the previous head's last tile, where q is no longer read
+  frag qf[ROWS][2];
+  auto load_q = [&](int h) {
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const T* qrow = (const T*)a.q + line_of(r) * tok_line + ((size_t)h * P + j) * HD + 8 * hh;
       qf[r][0] = gld8<T>(qrow);
       qf[r][1] = gld8<T>(qrow + 16);
+    }
+  };
+  load_q(0);
+#pragma unroll 1
+  for (int h = 0; h < NH; ++h) {
+    f32x16 o[ROWS];
+    f32x4 lacc[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
       o[r] = zero;
       lacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -1395,6 +1403,9 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       for (int i = 0; i < 6; ++i) { TA_SGB(0x008, 1); TA_SGB(0x002, 6); }
       TA_FENCE();
       // phase 3: scores of the next tile's chunk 0, P.V of chunk 2 | exponentials of chunk 3
+      if constexpr (LAST) {
+        if (h + 1 < NH) load_q(h + 1);             // the next head's q (this head's is done)
+      }
       if constexpr (!LAST) kfr(nxt, 0, kfb);
       vfr(cur, 3, vf_last);
       if constexpr (!LAST) s_first = score(0, kfb, b_nxt);
