@@ -899,17 +899,26 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
     __syncthreads();
   }
 
-#pragma unroll 1
-  for (int h = 0; h < NH; ++h) {
-    frag qf[ROWS][2], qm[ROWS];
-    float m[ROWS], lsum[ROWS];
-    bool mact[ROWS];                               // wave-uniform: some lane of the row has m != 0
-    f32x16 o[ROWS];
+  // q of head h; heads after the first are loaded during the previous head's last
+  // tile, once its score products have read q
+  frag qf[ROWS][2];
+  auto load_q = [&](int h) {
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const T* qrow = (const T*)a.q + line_of(r) * tok_line + ((size_t)h * P + j) * HD + 8 * hh;
       qf[r][0] = gld8<T>(qrow);
       qf[r][1] = gld8<T>(qrow + 16);
+    }
+  };
+  load_q(0);
+#pragma unroll 1
+  for (int h = 0; h < NH; ++h) {
+    frag qm[ROWS];
+    float m[ROWS], lsum[ROWS];
+    bool mact[ROWS];                               // wave-uniform: some lane of the row has m != 0
+    f32x16 o[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
       qm[r] = unit_frag<T>(0.f);
       m[r] = 0.f;
       mact[r] = false;
@@ -973,6 +982,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
           for (int st = 0; st < 2; ++st) sc[r][st] = mma(e0, qm[r], sc[r][st]);
         }
       }
+      if (kt == nbt - 1 && h + 1 < NH) load_q(h + 1);   // the next head's q (this head's is read)
       if (FIRST && !a.state_in) {                     // (a carried shift stands)
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
@@ -1044,6 +1054,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
 #pragma unroll
         for (int st = 0; st < 2; ++st) sc[r][st] = mma(kf[st][1], qf[r][1], sc[r][st]);
       }
+      if (kt == nbt - 1 && h + 1 < NH) load_q(h + 1);   // the next head's q (this head's is read)
       if constexpr (FIRST) {
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
