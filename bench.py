@@ -695,6 +695,12 @@ def main():
             torch.cuda.empty_cache()
         res["other_workloads"] = others
     res["gpu_clock"] = gpu_clock()
+    mhz = res["gpu_clock"]["sclk_mhz"]
+    if mhz and res["dtype"] == "bf16":
+        # the dense bf16 peak at the reported clock: 256 CUs x 4096 flops per cycle (2.5 PF at 2.4 GHz)
+        at_clock = 256 * 4096 * mhz * 1e6 / 1e12
+        res["roofline"]["peak_at_reported_clock"] = round(at_clock, 1)
+        res["roofline"]["frac_at_reported_clock"] = round(res["roofline"]["achieved"] / at_clock, 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, inputs.workload_z(wl), inputs.workload_weights(wl))
     print(json.dumps(res), flush=True)
