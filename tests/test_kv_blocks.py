@@ -134,13 +134,25 @@ def test_kv_block_final_single_block(dtype):
     check(out, ref.triangle_attn_start(inputs.to_f64(z), params64(w)), dtype, "kv final, one block")
 
 
+def fold_and_finish(ws, wd, I, R, dtype, variant, blocks, order, fused_last):
+    """Every block folded, then finalize; or the last one folded and finished in one launch."""
+    if not fused_last:
+        st = fold(ws, wd, I, R, dtype, variant, blocks, order)
+        return ta.triangle_attn_attend_finalize(ws, wd, I, R, TDT[dtype], st, variant=variant)
+    st = fold(ws, wd, I, R, dtype, variant, blocks, order[:-1])
+    kb, vb, bb, nk = blocks[order[-1]]
+    return ta.triangle_attn_attend_kv_block_final(ws, wd, I, R, TDT[dtype], kb, vb, bb, nk, len(order) == 1, st,
+                                                  variant=variant)
+
+
+@pytest.mark.parametrize("fused_last", [False, True])
 @pytest.mark.parametrize("order", [[0, 1, 2], [2, 0, 1]])
-def test_kv_blocks_rows_large_offsets(order):
+def test_kv_blocks_rows_large_offsets(order, fused_last):
     """Row block with a caller bias carrying per-query offsets of +-30 and keys
     0..63 a further 60 below: each block is packed with its own per-query shift,
-    which the state must carry across blocks."""
+    which the state must carry across blocks (into the last, fused call too)."""
     I, R = 257, 9
-    say(f"[kv blocks] rows I={I} R={R}, offsets +-30, order {order}")
+    say(f"[kv blocks] rows I={I} R={R}, offsets +-30, order {order}, fused last {fused_last}")
     w = weights_with_extras(700, "bf16")
     zr = inputs.make_z_rows(700, I, 3, R, "bf16")
     bias = inputs.random_bias(700, 4, I, scale=2.0, offset_per_query=np.linspace(-30, 30, I))
@@ -148,20 +160,20 @@ def test_kv_blocks_rows_large_offsets(order):
     wd = dev(w)
     ws = ta.triangle_attn_project(zr.cuda(), wd, variant="rows")
     blocks = cut_blocks(ws, I, R, "bf16", "rows", (64, 129, 64), bias.cuda())
-    st = fold(ws, wd, I, R, "bf16", "rows", blocks, order)
-    out = ta.triangle_attn_attend_finalize(ws, wd, I, R, torch.bfloat16, st, variant="rows")
+    out = fold_and_finish(ws, wd, I, R, "bf16", "rows", blocks, order, fused_last)
     torch.cuda.synchronize()
     check(out, ref.triangle_attn_rows(inputs.to_f64(zr), inputs.to_f64(bias), params64(w)), "bf16",
           "kv blocks, offsets")
 
 
+@pytest.mark.parametrize("fused_last", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("order", [[0, 1], [1, 0]])
-def test_kv_blocks_far_apart(dtype, order):
+def test_kv_blocks_far_apart(dtype, order, fused_last):
     """One block ~100 nats below the other: its keys either lift the carried maximum
     by ~144 (base 2) or underflow to zero weight, depending on the order."""
     I, R = 256, 16
-    say(f"[kv blocks] far-apart blocks, order {order}, {dtype}")
+    say(f"[kv blocks] far-apart blocks, order {order}, {dtype}, fused last {fused_last}")
     w = weights_with_extras(800, dtype)
     zr = inputs.make_z_rows(800, I, 0, R, dtype)
     bias = inputs.random_bias(800, 4, I, scale=1.0)
@@ -169,8 +181,7 @@ def test_kv_blocks_far_apart(dtype, order):
     wd = dev(w)
     ws = ta.triangle_attn_project(zr.cuda(), wd, variant="rows")
     blocks = cut_blocks(ws, I, R, dtype, "rows", (128, 128), bias.cuda())
-    st = fold(ws, wd, I, R, dtype, "rows", blocks, order)
-    out = ta.triangle_attn_attend_finalize(ws, wd, I, R, TDT[dtype], st, variant="rows")
+    out = fold_and_finish(ws, wd, I, R, dtype, "rows", blocks, order, fused_last)
     torch.cuda.synchronize()
     check(out, ref.triangle_attn_rows(inputs.to_f64(zr), inputs.to_f64(bias), params64(w)), dtype, "far apart")
 
