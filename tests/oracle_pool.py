@@ -23,7 +23,7 @@ def _limit_blas():
 
 
 def workers() -> int:
-    """Cores this process may use (the GPU machine's share), at most 16."""
+    """Cores in this process's affinity, at most 16 (one GPU's share of a host's cores)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
