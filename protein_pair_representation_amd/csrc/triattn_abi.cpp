@@ -182,7 +182,7 @@ int pack_bias(const ta_problem* p, int variant, const float* caller_bias, void* 
                                            p->dtype, s));
 }
 
-// Shared driver of start / end / rows.
+// Shared implementation of start / end / rows.
 int run_full(const ta_problem* p, int variant, const ta_weights* w, const void* z, const float* bias,
              void* out, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_problem(p, variant);
