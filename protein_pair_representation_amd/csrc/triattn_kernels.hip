@@ -728,42 +728,64 @@ __device__ __forceinline__ void map_block(int mode, int bid, int n_lg, int nqb, 
 
 // Output projection of a workgroup's rows: out^T[c][j] = sum_(h,e) W_o[c][h*32+e]
 // o^T[h*32+e][j] + b_o[c], from the gated head outputs in the workspace (this lane
-// reads back exactly the o values it wrote).  W_o is first staged into w_lds
-// (the K/V staging area, free once the key loop is over), so that the products
-// run back to back on register and LDS operands.
+// reads back exactly the o values it wrote).  W_o is staged into w_lds (the K/V
+// staging area, free once the key loop is over) and b_o into a small LDS array, so
+// that the products run back to back on register and LDS operands.  Every global
+// read (W_o, b_o, the head outputs of all rows) is issued before the first wait:
+// one memory latency for the whole projection instead of one per row and per
+// column tile (the output stores kept the compiler from hoisting the b_o loads).
 template <typename T, int ROWS, int NT>
 __device__ __forceinline__ void out_projection(const AttendArgs& a, int line0, int j, int hh, int lr, u32x4* w_lds) {
   typedef typename El<T>::frag frag;
   constexpr int WU = CZ * El<T>::bytes / 16;       // 16-B units per W_o row
+  constexpr int WN = CZ * WU / NT;                 // W_o units staged per thread
+  static_assert(CZ * WU % NT == 0 && CZ <= NT, "W_o / b_o staging split");
+  __shared__ float bo_lds[CZ];
   const int I = a.I, P = a.P;
   const size_t tok_line = (size_t)NH * P * HD;
-  __syncthreads();                                 // every wave is done with the K/V tiles
-  for (int idx = threadIdx.x; idx < CZ * WU; idx += NT) {
-    const int r = idx / WU, u = idx % WU;
-    lds_put<WU>(w_lds, r, u, reinterpret_cast<const u32x4*>((const T*)a.w_o + (size_t)r * CZ)[u]);
-  }
-  __syncthreads();
-#pragma unroll 1
+  u32x4 wreg[WN];
+#pragma unroll
+  for (int k = 0; k < WN; ++k) wreg[k] = reinterpret_cast<const u32x4*>(a.w_o)[threadIdx.x + k * NT];
+  const float bo = a.b_o != nullptr && threadIdx.x < CZ ? a.b_o[threadIdx.x] : 0.f;
+  frag of[ROWS][NH][2];
+#pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    if (line0 + r >= a.lines) break;
-    const int line = line0 + r;
+    const int line = line0 + r < a.lines ? line0 + r : a.lines - 1;   // a missing row is loaded, not used
     const T* orow_ws = (const T*)a.o + (size_t)line * tok_line + (size_t)j * HD + 16 * hh;
-    T* orow = (T*)a.out + (a.out_transposed ? ((size_t)j * I + line) : ((size_t)line * I + j)) * CZ;
-    frag of[NH][2];
 #pragma unroll
     for (int hd = 0; hd < NH; ++hd)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) of[hd][c] = gld8<T>(orow_ws + (size_t)hd * P * HD + 8 * c);
+      for (int c = 0; c < 2; ++c) of[r][hd][c] = gld8<T>(orow_ws + (size_t)hd * P * HD + 8 * c);
+  }
+  // LDS-only barriers: every wave is done with the K/V tiles, then W_o and b_o are
+  // in LDS; the head outputs stay in flight until the first product
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+  for (int k = 0; k < WN; ++k) {
+    const int idx = threadIdx.x + k * NT;
+    lds_put<WU>(w_lds, idx / WU, idx % WU, wreg[k]);
+  }
+  if (threadIdx.x < CZ) bo_lds[threadIdx.x] = bo;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    if (line0 + r >= a.lines) break;
+    const int line = line0 + r;
+    T* orow = (T*)a.out + (a.out_transposed ? ((size_t)j * I + line) : ((size_t)line * I + j)) * CZ;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       f32x16 acc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = a.b_o ? a.b_o[32 * ct + 16 * hh + i] : 0.f;
+      for (int i = 0; i < 16; ++i) acc[i] = bo_lds[32 * ct + 16 * hh + i];
 #pragma unroll
       for (int hd = 0; hd < NH; ++hd)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          acc = mma(lds_frag<T, WU>(w_lds, 32 * ct + rho(lr), 4 * hd + 2 * hh + c), of[hd][c], acc);
+          acc = mma(lds_frag<T, WU>(w_lds, 32 * ct + rho(lr), 4 * hd + 2 * hh + c), of[r][hd][c], acc);
       if (j < I) {
         float ov[16];
 #pragma unroll
@@ -1123,14 +1145,23 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       }
       continue;
     }
-    // ---- finish head h: 1/l, gate; o^T (e = 16*hh + i) to the workspace
+    // ---- finish head h: 1/l, gate; o^T (e = 16*hh + i) to the workspace.  The
+    // gates of all rows are loaded before the first store (a store keeps the compiler
+    // from hoisting a later row's loads above it): one memory latency per head
+    frag gf[ROWS][2];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const size_t tok = line_of(r) * tok_line + ((size_t)h * P + j) * HD + 16 * hh;
+      gf[r][0] = gld8<T>((const T*)a.g + tok);
+      gf[r][1] = gld8<T>((const T*)a.g + tok + 8);
+    }
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const float inv = 1.0f / xhalf_sum(lsum[r]);
       const size_t tok = line_of(r) * tok_line + ((size_t)h * P + j) * HD + 16 * hh;
       float gv[16];
-      frag_to_f32<T>(gld8<T>((const T*)a.g + tok), gv);
-      frag_to_f32<T>(gld8<T>((const T*)a.g + tok + 8), gv + 8);
+      frag_to_f32<T>(gf[r][0], gv);
+      frag_to_f32<T>(gf[r][1], gv + 8);
       float ov[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) ov[i] = o[r][i] * inv * gv[i];
@@ -1470,6 +1501,14 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
     }
 
     // ---- finish head h: row sums, 1/l, gate; o^T (e = 16*hh + i) to the workspace
+    // (the gates of both rows loaded first, as in tri_attend)
+    frag gf[ROWS][2];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const size_t tok = line_of(r) * tok_line + ((size_t)h * P + j) * HD + 16 * hh;
+      gf[r][0] = gld8<T>((const T*)a.g + tok);
+      gf[r][1] = gld8<T>((const T*)a.g + tok + 8);
+    }
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const float lsum = __shfl(lacc[r][0], rs_src);
@@ -1477,8 +1516,8 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       const float inv = 1.0f / lsum;
       const size_t tok = line_of(r) * tok_line + ((size_t)h * P + j) * HD + 16 * hh;
       float gv[16];
-      frag_to_f32<T>(gld8<T>((const T*)a.g + tok), gv);
-      frag_to_f32<T>(gld8<T>((const T*)a.g + tok + 8), gv + 8);
+      frag_to_f32<T>(gf[r][0], gv);
+      frag_to_f32<T>(gf[r][1], gv + 8);
       float ov[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) ov[i] = o[r][i] * inv * gv[i];
