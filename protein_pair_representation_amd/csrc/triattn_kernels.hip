@@ -730,67 +730,91 @@ __device__ __forceinline__ void map_block(int mode, int bid, int n_lg, int nqb, 
 // o^T[h*32+e][j] + b_o[c], from the gated head outputs in the workspace (this lane
 // reads back exactly the o values it wrote).  W_o is staged into w_lds (the K/V
 // staging area, free once the key loop is over) and b_o into a small LDS array, so
-// that the products run back to back on register and LDS operands.  Every global
-// read (W_o, b_o, the head outputs of all rows) is issued before the first wait:
-// one memory latency for the whole projection instead of one per row and per
-// column tile (the output stores kept the compiler from hoisting the b_o loads).
+// that the products run back to back on register and LDS operands.
+//  * Every global read (W_o, b_o, the head outputs of all rows) is issued before the
+//    first wait: one memory latency for the whole projection.
+//  * The lane's indices are recomputed here from an opaque copy of the thread id, and
+//    every address is formed before the first load (a scheduling fence between).
+//    Values kept from the start of the kernel would have been spilled over the key
+//    loop, and a scratch reload counts in the same in-order vmcnt as the loads: a
+//    reload between the loads makes the wave wait for all loads issued before it.
+// j0 is the workgroup's first query (its waves take 32 queries each).
 template <typename T, int ROWS, int NT>
-__device__ __forceinline__ void out_projection(const AttendArgs& a, int line0, int j, int hh, int lr, u32x4* w_lds) {
+__device__ __forceinline__ void out_projection(const AttendArgs& a, int line0, int j0, u32x4* w_lds) {
   typedef typename El<T>::frag frag;
   constexpr int WU = CZ * El<T>::bytes / 16;       // 16-B units per W_o row
   constexpr int WN = CZ * WU / NT;                 // W_o units staged per thread
   static_assert(CZ * WU % NT == 0 && CZ <= NT, "W_o / b_o staging split");
   __shared__ float bo_lds[CZ];
+  unsigned tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));                    // a new value: nothing derived from it is reused
+  const int lane = tid & 63, hh = lane >> 5, lr = lane & 31;
+  const int j = j0 + (int)(tid >> 6) * 32 + lr;
   const int I = a.I, P = a.P;
   const size_t tok_line = (size_t)NH * P * HD;
-  u32x4 wreg[WN];
+  int wdst[WN];
 #pragma unroll
-  for (int k = 0; k < WN; ++k) wreg[k] = reinterpret_cast<const u32x4*>(a.w_o)[threadIdx.x + k * NT];
-  const float bo = a.b_o != nullptr && threadIdx.x < CZ ? a.b_o[threadIdx.x] : 0.f;
-  frag of[ROWS][NH][2];
+  for (int k = 0; k < WN; ++k) {
+    const int idx = (int)tid + k * NT, r = idx / WU, u = idx % WU;
+    wdst[k] = r * WU + (u ^ swz<WU>(r));
+  }
+  const u32x4* wsrc = reinterpret_cast<const u32x4*>(a.w_o) + tid;
+  const T* orow_ws[ROWS];
+  T* orow[ROWS];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     const int line = line0 + r < a.lines ? line0 + r : a.lines - 1;   // a missing row is loaded, not used
-    const T* orow_ws = (const T*)a.o + (size_t)line * tok_line + (size_t)j * HD + 16 * hh;
+    orow_ws[r] = (const T*)a.o + (size_t)line * tok_line + (size_t)j * HD + 16 * hh;
+    orow[r] = (T*)a.out + (a.out_transposed ? ((size_t)j * I + line) : ((size_t)line * I + j)) * CZ + 16 * hh;
+  }
+  const int arow = rho(lr);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 wreg[WN];
+#pragma unroll
+  for (int k = 0; k < WN; ++k) wreg[k] = wsrc[k * NT];
+  const float bo = a.b_o != nullptr && tid < CZ ? a.b_o[tid] : 0.f;
+  frag of[ROWS][NH][2];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r)
 #pragma unroll
     for (int hd = 0; hd < NH; ++hd)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) of[r][hd][c] = gld8<T>(orow_ws + (size_t)hd * P * HD + 8 * c);
-  }
+      for (int c = 0; c < 2; ++c) of[r][hd][c] = gld8<T>(orow_ws[r] + (size_t)hd * P * HD + 8 * c);
   // LDS-only barriers: every wave is done with the K/V tiles, then W_o and b_o are
   // in LDS; the head outputs stay in flight until the first product
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 #pragma unroll
-  for (int k = 0; k < WN; ++k) {
-    const int idx = threadIdx.x + k * NT;
-    lds_put<WU>(w_lds, idx / WU, idx % WU, wreg[k]);
-  }
-  if (threadIdx.x < CZ) bo_lds[threadIdx.x] = bo;
+  for (int k = 0; k < WN; ++k) w_lds[wdst[k]] = wreg[k];
+  if (tid < CZ) bo_lds[tid] = bo;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  // column tiles outside, rows inside: a tile's W_o fragments are read from LDS once
+  // and serve every row
 #pragma unroll
-  for (int r = 0; r < ROWS; ++r) {
-    if (line0 + r >= a.lines) break;
-    const int line = line0 + r;
-    T* orow = (T*)a.out + (a.out_transposed ? ((size_t)j * I + line) : ((size_t)line * I + j)) * CZ;
+  for (int ct = 0; ct < 4; ++ct) {
+    frag wf[NH][2];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int hd = 0; hd < NH; ++hd)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) wf[hd][c] = lds_frag<T, WU>(w_lds, 32 * ct + arow, 4 * hd + 2 * hh + c);
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      if (line0 + r >= a.lines) break;
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = bo_lds[32 * ct + 16 * hh + i];
 #pragma unroll
       for (int hd = 0; hd < NH; ++hd)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          acc = mma(lds_frag<T, WU>(w_lds, 32 * ct + rho(lr), 4 * hd + 2 * hh + c), of[r][hd][c], acc);
+        for (int c = 0; c < 2; ++c) acc = mma(wf[hd][c], of[r][hd][c], acc);
       if (j < I) {
         float ov[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) ov[i] = acc[i];
-        T* p = orow + 32 * ct + 16 * hh;
+        T* p = orow[r] + 32 * ct;
         gst8<T>(p, to_frag<T>(ov));
         gst8<T>(p + 8, to_frag<T>(ov + 8));
       }
@@ -1179,7 +1203,7 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
     if (redo) return;                              // the shifted form redoes this workgroup
   }
   static_assert(2 * STAGE_UNITS >= CZ * CZ * El<T>::bytes / 16, "W_o must fit in the K/V staging area");
-  if (!a.state_out) out_projection<T, ROWS, NT>(a, line0, j, hh, lr, &kv_lds[0][0]);
+  if (!a.state_out) out_projection<T, ROWS, NT>(a, line0, qb * QBW, &kv_lds[0][0]);
 }
 
 // ================================================================ K2: bf16 one-pass form
@@ -1532,7 +1556,7 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
   if (tid == 0) a.redo[blockIdx.x] = redo ? 1 : 0;
   if (redo) return;
   static_assert(NSLOT * STAGE_UNITS >= CZ * CZ * 2 / 16, "W_o must fit in the K/V staging area");
-  out_projection<T, ROWS, NT>(a, line0, j, hh, lr, kv_lds);
+  out_projection<T, ROWS, NT>(a, line0, qb * QBW, kv_lds);
 }
 
 // Bias pack: natural-log fp32 bias [H][Q][K] (from K1 or the caller: Q query rows,
