@@ -1222,6 +1222,8 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
 //    latency), and each chunk's bias is converted into its score accumulator.
 //  * Row sums come from the matrix core (v_mfma_f32_16x16x32_bf16 with a 0/1
 //    operand, below) instead of 32 dot products per tile on the VALU.
+//  * A head's last tile loads, in its last phase, the next head's q and this head's
+//    gates, so the head epilogue and the next head's first scores find them there.
 // Semantics, workgroup grid, redo flags and epilogue are those of tri_attend's
 // unshifted form.
 
@@ -1403,11 +1405,21 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
     // and P and the V^T fragments of this tile's chunk 3
     f32x16 s_first;
     frag pf_last[2], vf_last[2];
+    frag gf[ROWS][2];                              // the head's gates, loaded in its last tile
 
     auto tile = [&](auto first_tag, auto last_tag) {
       constexpr bool FIRST = decltype(first_tag)::value;   // first key tile of the head
       constexpr bool LAST = decltype(last_tag)::value;     // last key tile of the head
       bfrag b_far[4];                              // bias of step g + 2
+      // the gates' addresses are formed before the tile's loads are issued: a base the
+      // register allocator spilled is then reloaded with no prefetch in flight (a
+      // scratch reload among the prefetches would make the wave wait for all of them)
+      const T* gp[ROWS];
+      if constexpr (LAST) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) gp[r] = (const T*)a.g + line_of(r) * tok_line + ((size_t)h * P + j) * HD + 16 * hh;
+        TA_FENCE();
+      }
       // K/V first: the wait for them at the end of the tile then leaves these
       // bias loads in flight (first used in the last phase of the next tile)
       load_tile(h2, kt0 + kt2);
@@ -1471,6 +1483,11 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
       // phase 3: scores of the next tile's chunk 0, P.V of chunk 2 | exponentials of chunk 3
       if constexpr (LAST) {
         if (h + 1 < NH) load_q(h + 1);             // the next head's q (this head's is done)
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {           // this head's gates, used after the tile
+          gf[r][0] = gld8<T>(gp[r]);
+          gf[r][1] = gld8<T>(gp[r] + 8);
+        }
       }
       if constexpr (!LAST) kfr(nxt, 0, kfb);
       vfr(cur, 3, vf_last);
@@ -1525,14 +1542,6 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
     }
 
     // ---- finish head h: row sums, 1/l, gate; o^T (e = 16*hh + i) to the workspace
-    // (the gates of both rows loaded first, as in tri_attend)
-    frag gf[ROWS][2];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const size_t tok = line_of(r) * tok_line + ((size_t)h * P + j) * HD + 16 * hh;
-      gf[r][0] = gld8<T>((const T*)a.g + tok);
-      gf[r][1] = gld8<T>((const T*)a.g + tok + 8);
-    }
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const float lsum = __shfl(lacc[r][0], rs_src);
