@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TRIATTN_ABI_VERSION 6
+#define TRIATTN_ABI_VERSION 7
 
 /* Compute dtypes. */
 enum { TA_BF16 = 1, TA_F32 = 2 };
@@ -206,9 +206,12 @@ int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* 
  * arrive in blocks (the 2D grid sharding of the Design-CP summary,
  * Methodology section 1, passes K/V blocks around; the softmax over keys is
  * then merged from partial states, as ring attention computes scores on the
- * fly).  For every (line, head, query) of the workspace a state is carried in
- * fp32: the shift m (base-2 units), the sum l of exp2(score - m) and the
- * unnormalised output O = sum exp2(score - m) v.  A call folds keys
+ * fly).  For every (line, head, query) of the workspace a state is carried:
+ * the shift m (base-2 units) and the sum l of exp2(score - m), in fp32, and the
+ * normalised output O / l, where O = sum exp2(score - m) v, in the dtype of the
+ * packed bias: fp16 for TA_BF16 problems (O / l is a convex combination of value
+ * vectors, so it lies within their range; values beyond +-65504 are not
+ * representable in this state), fp32 for TA_F32.  A call folds keys
  * [key0, key0 + nkeys) into it.  Blocks may come in any order; once every key
  * has been folded exactly once, triangle_attn_attend_finalize gives what
  * triangle_attn_attend gives (up to rounding).
@@ -218,14 +221,15 @@ int triangle_attn_attend(const ta_problem* prob, int variant, const ta_weights* 
  *           TA_ROWS the caller's fp32 bias [H][I][I] is packed into the
  *           workspace by this call (bias required).  Zero: the state carries the
  *           earlier blocks, bias is ignored (may be NULL)
- *   state   fp32, triangle_attn_state_bytes() bytes: O [L][H][P][d], then at the
- *           next 256-byte boundary (m, l) [L][H][P][2] (L, P as in the layout),
- *           then at the next one [H][P] of scratch for caller-held blocks
+ *   state   triangle_attn_state_bytes() bytes, 16-byte aligned: O / l
+ *           [L][H][P][d] (fp16 for TA_BF16, fp32 for TA_F32), then at the next
+ *           256-byte boundary (m, l) fp32 [L][H][P][2] (L, P as in the layout),
+ *           then at the next one fp32 [H][P] of scratch for caller-held blocks
  *   ws      filled by triangle_attn_project with the same problem and variant */
 int triangle_attn_state_bytes(const ta_problem* prob, int variant, size_t* bytes);
 int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_weights* w,
                                const float* bias, int32_t key0, int32_t nkeys, int32_t first,
-                               float* state, void* ws, size_t ws_bytes, void* stream);
+                               void* state, void* ws, size_t ws_bytes, void* stream);
 
 /* Key-block stage on a block the caller holds: the ring step of that sharding.
  * The device keeps its queries (q and the gate, in `ws`, from
@@ -236,8 +240,8 @@ int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_wei
  * triangle_attn_attend_block does for a key range of the workspace; blocks may
  * come in any order, and once every key has been folded exactly once
  * triangle_attn_attend_finalize gives what triangle_attn_attend gives (up to
- * rounding).  To fold several blocks in one call (the fp32 state is read and
- * written once per call), place them side by side in one buffer.
+ * rounding).  To fold several blocks in one call (the state is read and written
+ * once per call), place them side by side in one buffer.
  *   k_blk        compute dtype [L][H][kv_positions][d]: key position p of line
  *                l, head h; positions >= nkeys are padding (finite values)
  *   vt_blk       compute dtype [L][H][d][kv_positions]: the values, transposed
@@ -261,13 +265,13 @@ int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_wei
 int triangle_attn_attend_kv_block(const ta_problem* prob, int variant, const ta_weights* w,
                                   const void* k_blk, const void* vt_blk, int32_t kv_positions,
                                   const float* bias_blk, int32_t nkeys, int32_t first,
-                                  float* state, void* ws, size_t ws_bytes, void* stream);
+                                  void* state, void* ws, size_t ws_bytes, void* stream);
 
 /* The last step of a ring: folds the last caller-held block into the carried
  * state and finishes the rows (o = O / l, gate, output projection) into `out`,
  * in one launch: what triangle_attn_attend_kv_block followed by
- * triangle_attn_attend_finalize computes, without writing the fp32 state and
- * reading it back.  The state is read (unless `first`, which makes this block
+ * triangle_attn_attend_finalize computes, without writing the state and reading
+ * it back.  The state is read (unless `first`, which makes this block
  * the only one) and is not updated, except for its scratch tail.  Arguments as
  * for triangle_attn_attend_kv_block, plus out as in triangle_attn_attend (rows x
  * I x c_z in the compute dtype, or transposed for TA_END); it also writes the
@@ -277,7 +281,7 @@ int triangle_attn_attend_kv_block(const ta_problem* prob, int variant, const ta_
 int triangle_attn_attend_kv_block_final(const ta_problem* prob, int variant, const ta_weights* w,
                                         const void* k_blk, const void* vt_blk, int32_t kv_positions,
                                         const float* bias_blk, int32_t nkeys, int32_t first,
-                                        float* state, void* out, void* ws, size_t ws_bytes,
+                                        void* state, void* out, void* ws, size_t ws_bytes,
                                         void* stream);
 
 /* triangle_attn_start without a workspace argument and without any allocation,
@@ -299,10 +303,10 @@ int triangle_attn_attend_kv_block_final(const ta_problem* prob, int variant, con
 int triangle_attn_start_noalloc(const ta_problem* prob, const ta_weights* w, const void* z,
                                 void* out, void* stream);
 
-/* Finish a key-block accumulation: o = O / l, sigmoid gate, output projection,
- * out as in triangle_attn_attend.  Writes the workspace's `o` region. */
+/* Finish a key-block accumulation: o = O / l (as carried), sigmoid gate, output
+ * projection, out as in triangle_attn_attend.  Writes the workspace's `o` region. */
 int triangle_attn_attend_finalize(const ta_problem* prob, int variant, const ta_weights* w,
-                                  const float* state, void* out, void* ws, size_t ws_bytes,
+                                  const void* state, void* out, void* ws, size_t ws_bytes,
                                   void* stream);
 
 #ifdef __cplusplus

@@ -164,8 +164,9 @@ triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weigh
 // State of the key-block stage: O [L][H][P][d] fp32, then (m, l) [L][H][P][2] fp32,
 // then the per-(head, query) shift [H][P] fp32 of the last caller-held block's
 // packed bias (written by that call's pack, read by its attention launch).
-void state_sizes(const ta_ws_layout& l, size_t* o_bytes, size_t* total, size_t* shift_off = nullptr) {
-  *o_bytes = align256((size_t)l.lines * kHeads * l.positions * kHeadDim * sizeof(float));
+void state_sizes(const ta_ws_layout& l, int dtype, size_t* o_bytes, size_t* total, size_t* shift_off = nullptr) {
+  const size_t oes = dtype == TA_BF16 ? 2 : 4;     // O / l in the bias dtype: fp16 or fp32
+  *o_bytes = align256((size_t)l.lines * kHeads * l.positions * kHeadDim * oes);
   const size_t sh = *o_bytes + align256((size_t)l.lines * kHeads * l.positions * 2 * sizeof(float));
   if (shift_off) *shift_off = sh;
   *total = sh + align256((size_t)kHeads * l.positions * sizeof(float));
@@ -391,12 +392,12 @@ int triangle_attn_state_bytes(const ta_problem* prob, int variant, size_t* bytes
   ta_ws_layout l;
   layout_of(prob, variant, &l);
   size_t ob;
-  state_sizes(l, &ob, bytes);
+  state_sizes(l, prob->dtype, &ob, bytes);
   return TA_OK;
 }
 
 int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_weights* w, const float* bias,
-                               int32_t key0, int32_t nkeys, int32_t first, float* state, void* ws,
+                               int32_t key0, int32_t nkeys, int32_t first, void* state, void* ws,
                                size_t ws_bytes, void* stream) {
   int rc = check_problem(prob, variant);
   if (rc) return rc;
@@ -413,7 +414,7 @@ int triangle_attn_attend_block(const ta_problem* prob, int variant, const ta_wei
   layout_of(prob, variant, &l);
   if (ws_bytes < l.total) return TA_ERR_WORKSPACE_TOO_SMALL;
   size_t ob, sb;
-  state_sizes(l, &ob, &sb);
+  state_sizes(l, prob->dtype, &ob, &sb);
   const Span bspan = {pack ? bias : nullptr, pack ? (size_t)kHeads * I * I * sizeof(float) : 0};
   if ((rc = check_out_alias(prob, w, {state, sb}, {nullptr, 0}, {ws, l.total}, bspan))) return rc;
   (void)hipGetLastError();
@@ -436,7 +437,7 @@ namespace {
 // shifted attention form folds it into the state (out == nullptr) or, for the last
 // block, folds it and finishes the rows into out without writing the state.
 int kv_block(const ta_problem* prob, int variant, const ta_weights* w, const void* k_blk, const void* vt_blk,
-             int32_t kv_positions, const float* bias_blk, int32_t nkeys, int32_t first, float* state, void* out,
+             int32_t kv_positions, const float* bias_blk, int32_t nkeys, int32_t first, void* state, void* out,
              void* ws, size_t ws_bytes, void* stream) {
   int rc = check_problem(prob, variant);
   if (rc) return rc;
@@ -455,7 +456,7 @@ int kv_block(const ta_problem* prob, int variant, const ta_weights* w, const voi
     return TA_ERR_BAD_SHAPE;
   if (ws_bytes < l.total) return TA_ERR_WORKSPACE_TOO_SMALL;
   size_t ob, sb, shift_off;
-  state_sizes(l, &ob, &sb, &shift_off);
+  state_sizes(l, prob->dtype, &ob, &sb, &shift_off);
   const size_t es = esize(prob->dtype);
   const size_t kv_bytes = (size_t)l.lines * kHeads * kv_positions * kHeadDim * es;
   const Span kspan = {k_blk, kv_bytes}, vspan = {vt_blk, kv_bytes};
@@ -496,21 +497,21 @@ extern "C" {
 
 int triangle_attn_attend_kv_block(const ta_problem* prob, int variant, const ta_weights* w, const void* k_blk,
                                   const void* vt_blk, int32_t kv_positions, const float* bias_blk, int32_t nkeys,
-                                  int32_t first, float* state, void* ws, size_t ws_bytes, void* stream) {
+                                  int32_t first, void* state, void* ws, size_t ws_bytes, void* stream) {
   return kv_block(prob, variant, w, k_blk, vt_blk, kv_positions, bias_blk, nkeys, first, state, nullptr, ws,
                   ws_bytes, stream);
 }
 
 int triangle_attn_attend_kv_block_final(const ta_problem* prob, int variant, const ta_weights* w,
                                         const void* k_blk, const void* vt_blk, int32_t kv_positions,
-                                        const float* bias_blk, int32_t nkeys, int32_t first, float* state,
+                                        const float* bias_blk, int32_t nkeys, int32_t first, void* state,
                                         void* out, void* ws, size_t ws_bytes, void* stream) {
   if (out == nullptr) return TA_ERR_NULL_PTR;
   return kv_block(prob, variant, w, k_blk, vt_blk, kv_positions, bias_blk, nkeys, first, state, out, ws,
                   ws_bytes, stream);
 }
 
-int triangle_attn_attend_finalize(const ta_problem* prob, int variant, const ta_weights* w, const float* state,
+int triangle_attn_attend_finalize(const ta_problem* prob, int variant, const ta_weights* w, const void* state,
                                   void* out, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_problem(prob, variant);
   if (rc) return rc;
@@ -521,13 +522,13 @@ int triangle_attn_attend_finalize(const ta_problem* prob, int variant, const ta_
   layout_of(prob, variant, &l);
   if (ws_bytes < l.total) return TA_ERR_WORKSPACE_TOO_SMALL;
   size_t ob, sb;
-  state_sizes(l, &ob, &sb);
+  state_sizes(l, prob->dtype, &ob, &sb);
   const size_t tok_bytes = (size_t)prob->rows * prob->I * kCz * esize(prob->dtype);
   if ((rc = check_out_alias(prob, w, {out, tok_bytes}, {nullptr, 0}, {ws, l.total}, {state, sb}))) return rc;
   (void)hipGetLastError();
   triattn::AttendArgs a = attend_args(prob, variant, w, nullptr, out, ws, l);
   a.nbt = 0;  // no keys: gate and output projection of the carried state
-  a.state_o = (float*)state;
+  a.state_o = const_cast<void*>(state);
   a.state_ml = (float*)((const char*)state + ob);
   a.state_in = 1;
   a.state_out = 0;

@@ -43,8 +43,9 @@ struct AttendArgs {
   int out_transposed;     // 1: out[j][line], 0: out[line][j]
   // key range: tiles kt0 .. kt0+nbt-1 of 64 keys (the whole row: 0, ceil(I/64))
   int kt0, nbt;
-  // carried softmax state (key-block mode): O [lines][H][P][d] and (m, l) [lines][H][P][2], fp32
-  float* state_o;
+  // carried softmax state (key-block mode): O / l [lines][H][P][d] in the bias dtype
+  // (fp16 for bf16 problems, fp32 for fp32) and (m, l) [lines][H][P][2] fp32
+  void* state_o;
   float* state_ml;
   int state_in;           // 1: start every head from the state instead of empty
   int state_out;          // 1: store the state at the end of every head (no gate, no output projection)

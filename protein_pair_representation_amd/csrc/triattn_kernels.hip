@@ -163,6 +163,41 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The carried O / l of the key-block state: 16 consecutive values of one lane, fp16
+// for bf16 problems (the bias dtype), fp32 for fp32 problems.
+template <typename S> __device__ __forceinline__ void state_o_load(const S* p, float (&v)[16]);
+template <> __device__ __forceinline__ void state_o_load<_Float16>(const _Float16* p, float (&v)[16]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const f16x8 h = *reinterpret_cast<const f16x8*>(p + 8 * c);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[8 * c + t] = (float)h[t];
+  }
+}
+template <> __device__ __forceinline__ void state_o_load<float>(const float* p, float (&v)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 f = reinterpret_cast<const f32x4*>(p)[q];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[4 * q + t] = f[t];
+  }
+}
+template <typename S> __device__ __forceinline__ void state_o_store(S* p, const float (&v)[16]);
+template <> __device__ __forceinline__ void state_o_store<_Float16>(_Float16* p, const float (&v)[16]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    f16x8 h;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) h[t] = (_Float16)v[8 * c + t];
+    *reinterpret_cast<f16x8*>(p + 8 * c) = h;
+  }
+}
+template <> __device__ __forceinline__ void state_o_store<float>(float* p, const float (&v)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    reinterpret_cast<f32x4*>(p)[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float sigmoidf_(float x) {
   return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * LOG2E));
@@ -972,21 +1007,20 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
       o[r] = zero;
       if (!UNSHIFTED && a.state_in) {
         // carried state: shift m (true units), sum l (held by the lower half) and
-        // unnormalised O.  This call's scores carry its bias's shift c, so it runs
-        // with m' = m - c rounded to the compute dtype (the MFMA subtracts m'
-        // exactly); O and l are rescaled by the rounding residual 2^((m - c) - m').
+        // O / l (stored normalised, in the bias dtype; O = (O / l) * l).  This call's
+        // scores carry its bias's shift c, so it runs with m' = m - c rounded to the
+        // compute dtype (the MFMA subtracts m' exactly); O and l are rescaled by the
+        // rounding residual 2^((m - c) - m').
         const size_t sq = ((size_t)line_of(r) * NH + h) * P + j;
         const float2 ml = *reinterpret_cast<const float2*>(a.state_ml + 2 * sq);
-        const f32x4* so = reinterpret_cast<const f32x4*>(a.state_o + sq * HD + 16 * hh);
         const float mt = ml.x - (a.bias_shift ? a.bias_shift[(size_t)h * P + j] : 0.f);
         const float me = (float)(T)mt;
         const float alpha = fast_exp2(mt - me);
+        float on[16];                              // the carried O / l
+        state_o_load<BT>(reinterpret_cast<const BT*>(a.state_o) + sq * HD + 16 * hh, on);
+        const float sc = ml.y * alpha;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 v = so[q4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) o[r][4 * q4 + t] = v[t] * alpha;
-        }
+        for (int t = 0; t < 16; ++t) o[r][t] = on[t] * sc;
         m[r] = me;
         lsum[r] = hh == 0 ? ml.y * alpha : 0.f;
         qm[r] = unit_frag<T>(hh == 0 ? -me : 0.f);
@@ -1155,15 +1189,18 @@ __global__ void __launch_bounds__(WAVES * 64, MIN_WAVES_PER_SIMD) tri_attend(Att
     }
 
     if (!UNSHIFTED && a.state_out) {
-      // ---- key-block mode: carry (m, l, O) to the next block
+      // ---- key-block mode: carry (m, l, O / l) to the next block (O / l is 0 where no
+      // key has weight yet)
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
         if (line0 + r >= a.lines) break;
         const size_t sq = ((size_t)(line0 + r) * NH + h) * P + j;
         const float lt = xhalf_sum(lsum[r]);
-        f32x4* so = reinterpret_cast<f32x4*>(a.state_o + sq * HD + 16 * hh);
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        float on[16];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) so[q4] = f32x4{o[r][4 * q4], o[r][4 * q4 + 1], o[r][4 * q4 + 2], o[r][4 * q4 + 3]};
+        for (int t = 0; t < 16; ++t) on[t] = o[r][t] * inv;
+        state_o_store<BT>(reinterpret_cast<BT*>(a.state_o) + sq * HD + 16 * hh, on);
         const float mt = m[r] + (a.bias_shift ? a.bias_shift[(size_t)h * P + j] : 0.f);
         if (hh == 0) *reinterpret_cast<float2*>(a.state_ml + 2 * sq) = make_float2(mt, lt);
       }

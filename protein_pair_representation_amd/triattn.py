@@ -278,7 +278,9 @@ def triangle_attn_state_bytes(I: int, rows: int, dtype: torch.dtype, variant: st
 
 
 def state(I: int, rows: int, dtype: torch.dtype, variant: str, device=None) -> torch.Tensor:
-    """A carried softmax state buffer for triangle_attn_attend_block (fp32, uninitialised)."""
+    """A carried softmax state buffer for triangle_attn_attend_block (uninitialised; held as
+    a float32 tensor of triangle_attn_state_bytes bytes: its regions have their own dtypes,
+    see state_views)."""
     n = triangle_attn_state_bytes(I, rows, dtype, variant)
     return torch.empty(n // 4, dtype=torch.float32, device=device or "cuda")
 
@@ -344,12 +346,16 @@ def triangle_attn_attend_finalize(ws, weights, I, rows, dtype, st, variant="star
 
 
 def state_views(st: torch.Tensor, I: int, rows: int, dtype: torch.dtype, variant: str) -> dict:
-    """O [L][H][P][d] and (m, l) [L][H][P][2] views of a state buffer."""
+    """O / l [L][H][P][d] (float16 for bf16 problems, float32 for fp32) and (m, l) [L][H][P][2]
+    (float32) views of a state buffer."""
     lay = triangle_attn_workspace_layout(I, rows, dtype, variant)
     L, P = lay.lines, lay.positions
     n_o = L * HEADS * P * HEAD_DIM
-    off_ml = ((n_o * 4 + 255) // 256 * 256) // 4
-    return {"O": st[:n_o].view(L, HEADS, P, HEAD_DIM), "ml": st[off_ml:off_ml + L * HEADS * P * 2].view(L, HEADS, P, 2)}
+    odt = torch.float16 if dtype == torch.bfloat16 else torch.float32
+    o_bytes = n_o * torch.tensor([], dtype=odt).element_size()
+    off_ml = ((o_bytes + 255) // 256 * 256) // 4
+    return {"O": st.view(odt)[:n_o].view(L, HEADS, P, HEAD_DIM),
+            "ml": st[off_ml:off_ml + L * HEADS * P * 2].view(L, HEADS, P, 2)}
 
 
 def workspace_views(ws: torch.Tensor, I: int, rows: int, dtype: torch.dtype, variant: str) -> dict:

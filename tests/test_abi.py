@@ -46,7 +46,7 @@ def test_exports_match_header(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.triangle_attn_abi_version() == 6
+    assert lib.triangle_attn_abi_version() == 7
     for code in range(0, -13, -1):
         msg = lib.triangle_attn_strerror(code).decode()
         assert msg and msg != "unknown error code"
@@ -179,13 +179,17 @@ def test_python_binding_rejects_cpu_tensors():
 
 
 def test_state_bytes(lib):
+    """O / l in the bias dtype (fp16 for bf16, fp32 for fp32), then (m, l) and the shift
+    scratch in fp32, each region starting at a 256-byte boundary."""
     n = ctypes.c_size_t()
-    p = prob(I=1000, dtype=ta.TA_BF16)
-    assert lib.triangle_attn_state_bytes(ctypes.byref(p), ta.TA_START, ctypes.byref(n)) == 0
     P = 1024
-    o = (1000 * 4 * P * 32 * 4 + 255) // 256 * 256
     ml = (1000 * 4 * P * 2 * 4 + 255) // 256 * 256
-    assert n.value == o + ml + 4 * P * 4                 # + the [H][P] shift scratch of caller-held blocks
+    for dt, es in [(ta.TA_BF16, 2), (ta.TA_F32, 4)]:
+        p = prob(I=1000, dtype=dt)
+        assert lib.triangle_attn_state_bytes(ctypes.byref(p), ta.TA_START, ctypes.byref(n)) == 0
+        o = (1000 * 4 * P * 32 * es + 255) // 256 * 256
+        assert n.value == o + ml + 4 * P * 4             # + the [H][P] shift scratch of caller-held blocks
+    p = prob(I=1000, dtype=ta.TA_BF16)
     assert lib.triangle_attn_state_bytes(ctypes.byref(p), ta.TA_START, None) == -1
     assert lib.triangle_attn_state_bytes(ctypes.byref(prob(I=64, rows=32)), ta.TA_START, ctypes.byref(n)) == -2
 

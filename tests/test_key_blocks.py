@@ -60,7 +60,8 @@ def test_blocks_match_oracle(variant, I, dtype, size, order):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_state_is_subset_attention(dtype):
-    """After one block, O / l is attention over that block's keys alone."""
+    """After one block, the carried O / l (fp16 for bf16 problems) is attention over that
+    block's keys alone."""
     I, keys = 257, (64, 128)
     say(f"[blocks] state after keys {keys[0]}..{keys[0] + keys[1] - 1} of I={I} {dtype}")
     w = weights_with_extras(400, dtype)
@@ -70,7 +71,7 @@ def test_state_is_subset_attention(dtype):
     st = run_blocks(ws, wd, I, I, dtype, "start", [keys], [0])
     torch.cuda.synchronize()
     v = ta.state_views(st, I, I, TDT[dtype], "start")
-    o_norm = (v["O"] / v["ml"][..., 1:2])[:, :, :I, :].permute(0, 2, 1, 3)   # [line][query][H][d]
+    o_norm = v["O"].float()[:, :, :I, :].permute(0, 2, 1, 3)               # O / l: [line][query][H][d]
     p = params64(w)
     z64 = inputs.to_f64(z)
     bias = ref.pair_bias(z64, p)
