@@ -219,3 +219,36 @@ def test_kv_blocks_workload_1024():
                                                  out.float().cpu().numpy(), range(I))
     say(f"    kv blocks I=1024 every token: max abs {maxabs:.3e}, rel L1 {rel:.3e}, non-finite {nonfin}")
     assert n == I * I * 128 and nonfin == 0 and maxabs <= 2e-2 and rel <= 5e-3
+
+
+@pytest.mark.timeout(900)
+def test_kv_blocks_sixteen_blocks_1024():
+    """A long ring: the I = 1024 workload as sixteen caller-held blocks of 64 keys in a
+    shuffled order, the last folded and finished in one launch.  For bf16 problems the
+    carried O / l is fp16 and is rounded once per fold, fifteen times here: 128 lines
+    (every query) against the oracle, and the whole output against one pass."""
+    wl = inputs.WORKLOADS["startend-bf16-I1024-distogram"]
+    order = ORDERS["shuffled"](16)
+    say(f"[kv blocks] startend-bf16-I1024-distogram start, 16 blocks of 64, order {order}")
+    w = inputs.workload_weights(wl)
+    z = inputs.workload_z(wl)
+    I = wl.I
+    wd = dev(w)
+    ws = ta.triangle_attn_project(z.cuda(), wd, variant="start")
+    one_pass = ta.triangle_attn_attend(ws, wd, I, I, torch.bfloat16, variant="start")
+    bias = ta.workspace_views(ws, I, I, torch.bfloat16, "start")["bias_f32"].clone()
+    blocks = cut_blocks(ws, I, I, "bf16", "start", (64,) * 16, bias)
+    st = fold(ws, wd, I, I, "bf16", "start", blocks, order[:-1])
+    out = torch.full((I, I, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kb, vb, bb, nk = blocks[order[-1]]
+    ta.triangle_attn_attend_kv_block_final(ws, wd, I, I, torch.bfloat16, kb, vb, bb, nk, False, st, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any(), "unwritten outputs"
+    check(out.cpu(), inputs.to_f64(one_pass), "bf16", "16 kv blocks vs one pass at I=1024")
+    p = params64(w)
+    z64 = inputs.to_f64(z)
+    lines = list(range(0, I, 8))
+    maxabs, rel, nonfin, n = oracle_pool.compare("start", z64, ref.pair_bias(z64, p), p,
+                                                 out.float().cpu().numpy(), lines)
+    say(f"    16 kv blocks I=1024, {len(lines)} lines: max abs {maxabs:.3e}, rel L1 {rel:.3e}, non-finite {nonfin}")
+    assert n == len(lines) * I * 128 and nonfin == 0 and maxabs <= 2e-2 and rel <= 5e-3
