@@ -7,6 +7,7 @@ never dereferences a pointer and makes no HIP call, so this runs without a GPU.
 import ctypes
 
 import pytest
+import torch
 
 from protein_pair_representation_amd import triattn as ta
 
@@ -192,6 +193,27 @@ def test_state_bytes(lib):
     p = prob(I=1000, dtype=ta.TA_BF16)
     assert lib.triangle_attn_state_bytes(ctypes.byref(p), ta.TA_START, None) == -1
     assert lib.triangle_attn_state_bytes(ctypes.byref(prob(I=64, rows=32)), ta.TA_START, ctypes.byref(n)) == -2
+
+
+@pytest.mark.parametrize("dtype,odt", [(torch.bfloat16, torch.float16), (torch.float32, torch.float32)])
+def test_state_views_layout(dtype, odt):
+    """The binding's typed views of a state buffer (a CPU tensor of the library's size)
+    sit where the header places them: O / l first in the bias dtype, (m, l) at the next
+    256-byte boundary, and the shift scratch after that within the buffer."""
+    I, rows = 200, 200
+    n = ta.triangle_attn_state_bytes(I, rows, dtype, "start")
+    st = torch.zeros(n // 4, dtype=torch.float32)
+    v = ta.state_views(st, I, rows, dtype, "start")
+    lay = ta.triangle_attn_workspace_layout(I, rows, dtype, "start")
+    L, P = lay.lines, lay.positions
+    assert v["O"].dtype == odt and v["O"].shape == (L, 4, P, 32)
+    assert v["ml"].dtype == torch.float32 and v["ml"].shape == (L, 4, P, 2)
+    base = st.data_ptr()
+    o_bytes = L * 4 * P * 32 * v["O"].element_size()
+    assert v["O"].data_ptr() == base
+    assert v["ml"].data_ptr() - base == (o_bytes + 255) // 256 * 256
+    ml_end = v["ml"].data_ptr() - base + L * 4 * P * 2 * 4
+    assert (ml_end + 255) // 256 * 256 + 4 * P * 4 == n       # the [H][P] shift scratch closes the buffer
 
 
 def test_block_rejects(lib):
