@@ -161,9 +161,10 @@ triattn::AttendArgs attend_args(const ta_problem* p, int variant, const ta_weigh
   return a;
 }
 
-// State of the key-block stage: O [L][H][P][d] fp32, then (m, l) [L][H][P][2] fp32,
-// then the per-(head, query) shift [H][P] fp32 of the last caller-held block's
-// packed bias (written by that call's pack, read by its attention launch).
+// State of the key-block stage: O / l [L][H][P][d] in the bias dtype (fp16 for bf16
+// problems, fp32 for fp32), then (m, l) [L][H][P][2] fp32, then the per-(head, query)
+// shift [H][P] fp32 of the last caller-held block's packed bias (written by that
+// call's pack, read by its attention launch); each region starts at a 256-B boundary.
 void state_sizes(const ta_ws_layout& l, int dtype, size_t* o_bytes, size_t* total, size_t* shift_off = nullptr) {
   const size_t oes = dtype == TA_BF16 ? 2 : 4;     // O / l in the bias dtype: fp16 or fp32
   *o_bytes = align256((size_t)l.lines * kHeads * l.positions * kHeadDim * oes);
