@@ -19,6 +19,14 @@ be built to the same parity bar.
 The same model, with the keys folded in blocks into a carried state as the key-block
 stage does, shows why that state holds O / l in fp16: over seven folds it costs about
 0.5% of relative L1 against an fp32 state, where a bf16 state would reach the bar.
+
+Two 16-bit alternatives are modelled as well.  The projection stage feeds the
+LayerNorm output x to the bf16 matrix core as hi + lo (two products per weight
+fragment): x rounded to bf16 alone costs about 25% more relative L1, while x and
+the weights in fp16 (one product) match the hi + lo split.  And the softmax
+operands in fp16 (scores rounded to fp16 before the exponential, P and v in fp16)
+would lower the error slightly; on gfx950 an fp16 exponential issues at the same
+rate as the fp32 one, so that variant would not be faster.
 """
 import numpy as np
 import pytest
@@ -218,3 +226,59 @@ def test_bf16_state_would_cost_more(case):
     _, rlb = errors(fold_model(z, p, 16, torch.bfloat16), want)
     print(f"block 16: fp16 state rel L1 {rl16:.3e}, bf16 state {rlb:.3e}")
     assert rlb > rl16, (rlb, rl16)
+
+
+def model16(z, p, xmode="hilo", w16=False, pv=torch.bfloat16, s16=False):
+    """Starting-node attention with the kernel's roundings and 16-bit alternatives:
+    xmode = "hilo" (the LayerNorm output seen to about fp32, as the hi + lo products do),
+    "bf16" or "fp16"; w16 rounds the projection weights to fp16 (the bf16 weights
+    convert exactly, up to fp16's range); pv is the dtype of P and v; s16 rounds
+    the scores to fp16 before the exponential (an fp16 exponential's input).  The
+    gate is projected from bf16 x unless x is fp16, as the projection kernel does."""
+    H, d = p["heads"], p["head_dim"]
+    x0 = ref.layer_norm(z, p["ln_gamma"], p["ln_beta"], p["eps"])
+    x = {"hilo": rnd(x0, torch.float32), "bf16": rnd(x0, torch.bfloat16), "fp16": rnd(x0, torch.float16)}[xmode]
+    xg = x if xmode == "fp16" else rnd(x0, torch.bfloat16)
+    W = {n: (rnd(p[n], torch.float16) if w16 else p[n]) for n in ("w_q", "w_k", "w_v", "w_g", "w_b")}
+    q = rnd(x @ W["w_q"].T * (LOG2E / np.sqrt(d)), torch.bfloat16)
+    k = rnd(x @ W["w_k"].T, torch.bfloat16)
+    v = rnd(x @ W["w_v"].T, pv)
+    g = rnd(ref.sigmoid(xg @ W["w_g"].T + p["b_g"]), torch.bfloat16)
+    b = np.moveaxis(x @ W["w_b"].T, -1, 0)
+    b = rnd((b - b.max(-1, keepdims=True)) * LOG2E, torch.float16)
+    out = []
+    for i in range(z.shape[0]):
+        heads = []
+        for h in range(H):
+            sl = slice(h * d, (h + 1) * d)
+            s = rnd(q[i, :, sl] @ k[i, :, sl].T + b[h], torch.float32)
+            if s16:
+                s = rnd(s, torch.float16)
+            pr = rnd(np.exp2(s), pv)
+            o = (pr @ v[i, :, sl]) / pr.sum(-1, keepdims=True)
+            heads.append(rnd(o * g[i, :, sl], torch.bfloat16))
+        out.append(rnd(np.concatenate(heads, -1) @ p["w_o"].T + p["b_o"], torch.bfloat16))
+    return np.stack(out)
+
+
+def test_projection_needs_more_than_bf16_x(case):
+    """x rounded to bf16 before the projections costs about 25% more relative L1 than
+    the hi + lo split the projection kernel uses (at I = 128 it sits at the bar); x
+    and the weights in fp16 with one product match the split."""
+    z, p, want = case
+    _, r_hilo = errors(model16(z, p, xmode="hilo"), want)
+    _, r_bf16 = errors(model16(z, p, xmode="bf16"), want)
+    mx16, r_fp16 = errors(model16(z, p, xmode="fp16", w16=True), want)
+    print(f"x hi+lo {r_hilo:.3e}, x bf16 {r_bf16:.3e}, x and W fp16 {r_fp16:.3e}")
+    assert r_bf16 > 1.15 * r_hilo, (r_bf16, r_hilo)
+    assert r_fp16 <= 1.02 * r_hilo and mx16 <= BAR_MAX_ABS, (r_fp16, r_hilo, mx16)
+
+
+def test_fp16_softmax_operands_hold_the_bar(case):
+    """Scores rounded to fp16 before the exponential, P and v in fp16: within the bar
+    and no worse than the bf16 P and v the kernel uses."""
+    z, p, want = case
+    _, r_bf16 = errors(model16(z, p), want)
+    mx, r_f16 = errors(model16(z, p, pv=torch.float16, s16=True), want)
+    print(f"P, v bf16 {r_bf16:.3e}; scores, P, v fp16 {r_f16:.3e} (max abs {mx:.2e})")
+    assert mx <= BAR_MAX_ABS and r_f16 <= r_bf16, (mx, r_f16, r_bf16)
