@@ -2,12 +2,15 @@
 //
 //   K1 tri_project : LayerNorm fused into one MFMA GEMM per token tile,
 //                    [tokens x 128] . [128 x (4*128 + 4)] -> q, k, v^T, g, pair bias.
-//   tri_pack_bias  : pair bias -> per-query shifted, base-2, compute-dtype tiles.
-//   K2 tri_attend  : fused attention per (line, block of 128 queries), all heads:
-//                    S^T = bias + K Q^T - m (bias and running maximum both added
-//                    by the MFMA itself, through selector fragments), online
-//                    softmax at wavefront level, O^T += V^T P^T, then 1/l, sigmoid
-//                    gate and the output projection, stored once.
+//   tri_pack_bias  : pair bias -> per-query shifted, base-2 tiles in the order of
+//                    the score accumulators (fp16 for bf16 problems, fp32 for fp32).
+//   K2 tri_attend  : fused attention per (line pair, block of 128 queries), all
+//                    heads: S^T = bias + K Q^T (- m), the bias widened into the
+//                    score accumulator and a running maximum m, when one is needed,
+//                    subtracted by the MFMA through a unit fragment; online softmax
+//                    at wavefront level, O^T += V^T P^T, then 1/l, sigmoid gate and
+//                    the output projection, stored once.  tri_attend_fast is its
+//                    one-pass bf16 form without m, with the row sums on the MFMA.
 //
 // Operator: gated triangular attention over the pair representation (named in
 // the LightNobel article, section 3.1; tokens of c_z = 128 channels, section 1.1).
@@ -48,8 +51,9 @@ constexpr int KT = 64;         // keys per attention tile
 constexpr int NTHREADS = 256;  // 4 waves
 constexpr float LOG2E = 1.4426950408889634f;
 // Masked / padded keys carry this bias (base-2 units): exp2 of it underflows to
-// exactly 0.  It must be finite: the bias enters the scores through a product
-// with a 0/1 selector, and 0 * -inf would be NaN.
+// exactly 0.  It must be finite: a row whose keys are all masked would otherwise
+// reach a running maximum of -inf, and the MFMA that subtracts it multiplies -m by
+// the zeros of a unit fragment (0 * inf is NaN).
 constexpr float MASKED = -30000.0f;
 
 // Word 3 of a raw (stride 0) gfx9 buffer resource: 32-bit data format, no
@@ -625,7 +629,8 @@ __global__ void __launch_bounds__(64 * ProjCfg<T>::WAVES) tri_project(ProjectArg
 // and the packed bias times log2(e), each query row of the bias shifted by its
 // own maximum (the softmax over keys is unchanged by a per-query shift).  After
 // that shift a score is bounded by |q||k|, so the tile softmax is just
-// p = exp2(acc), its conversion, and a row sum (dot2 on packed pairs).
+// p = exp2(acc), its conversion, and a row sum (dot2 on packed pairs here; the
+// one-pass bf16 kernel further down sums on the matrix core).
 // A running shift m is only introduced when needed: when the first tile of a
 // head has its maximum outside [-64, 64], or when a tile's partial sums pass
 // 2^64 (far from fp32 overflow).  Then the exact maximum is taken, O and l are
@@ -1615,16 +1620,20 @@ __global__ void __launch_bounds__(256, MIN_WAVES_PER_SIMD) tri_attend_fast(Atten
 // (base 2) goes to `shift` when the caller needs it (key blocks).  Keys >= K get
 // MASKED; values below MASKED (e.g. -inf, a masked key) are raised to it; padded
 // query rows Q..(Q rounded up to 32)-1 get 0 and a zero shift.
+// One wave per row (four rows per workgroup at once): the row maximum is a wave
+// reduction, with no barrier, and the second pass over the row reads what the first
+// one brought into the caches.  Four consecutive keys per lane: one 16-B read when
+// the row is 16-B aligned, and one contiguous run of the tiled layout to write.
 template <typename BT>
 __global__ void __launch_bounds__(NTHREADS) tri_pack_bias(const float* __restrict__ src, BT* __restrict__ dst,
                                                           int Q, int K, int P, int NB, int rows_pad,
                                                           float* __restrict__ shift) {
-  __shared__ float red[NTHREADS / 64];
-  for (int r = blockIdx.x; r < NH * rows_pad; r += gridDim.x) {
+  constexpr int WPB = NTHREADS / 64;  // rows in flight per workgroup
+  const int lane = threadIdx.x & 63;
+  const int nrows = NH * rows_pad;
+  for (int r = blockIdx.x * WPB + (threadIdx.x >> 6); r < nrows; r += gridDim.x * WPB) {
     const int h = r / rows_pad, j = r % rows_pad;
-    const float* s = src + ((size_t)h * Q + j) * K;
-    // four consecutive keys per thread: one 16-B read when the row is 16-B aligned,
-    // and one contiguous run of the tiled layout to write
+    const float* s = src + ((size_t)h * Q + (j < Q ? j : 0)) * K;
     const bool vec = (reinterpret_cast<uintptr_t>(s) & 15) == 0;
     auto load4 = [&](int k0, float (&v)[4]) {
       if (vec && k0 + 3 < K) {
@@ -1636,19 +1645,19 @@ __global__ void __launch_bounds__(NTHREADS) tri_pack_bias(const float* __restric
       }
     };
     float mx = -INFINITY;
-    if (j < Q)
-      for (int c = threadIdx.x; c < ((K + 3) >> 2); c += NTHREADS) {
+    if (j < Q) {
+#pragma unroll 4
+      for (int c = lane; c < ((K + 3) >> 2); c += 64) {
         float v[4];
         load4(c << 2, v);
         mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
       }
+    }
+#pragma unroll
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();  // red is reused by the next row
-    if (shift != nullptr && threadIdx.x == 0) shift[(size_t)h * P + j] = j < Q ? mx * LOG2E : 0.f;
-    for (int c = threadIdx.x; c < (NB >> 2); c += NTHREADS) {
+    if (shift != nullptr && lane == 0) shift[(size_t)h * P + j] = j < Q ? mx * LOG2E : 0.f;
+#pragma unroll 4
+    for (int c = lane; c < (NB >> 2); c += 64) {
       const int k0 = c << 2;
       float v[4] = {0.f, 0.f, 0.f, 0.f};
       if (j < Q) load4(k0, v);
@@ -1720,7 +1729,8 @@ hipError_t launch_project(const ProjectArgs& a, int dtype, hipStream_t stream) {
 hipError_t launch_pack_bias(const float* src, void* dst, int Q, int K, int P, int NB, float* shift, int dtype,
                             hipStream_t stream) {
   const int rows_pad = (Q + 31) & ~31;
-  int grid = NH * rows_pad < 8 * cu_count() ? NH * rows_pad : 8 * cu_count();
+  const int wgs = (NH * rows_pad + NTHREADS / 64 - 1) / (NTHREADS / 64);  // one wave per row
+  const int grid = wgs < 16 * cu_count() ? wgs : 16 * cu_count();
   if (dtype == 1)
     hipLaunchKernelGGL(tri_pack_bias<_Float16>, dim3((unsigned)grid), dim3(NTHREADS), 0, stream, src,
                        (_Float16*)dst, Q, K, P, NB, rows_pad, shift);
