@@ -41,19 +41,25 @@ def _part(task):
     return float(err.sum()), float(np.abs(want).sum()), float(err.max()), int((~finite).sum()), int(err.size)
 
 
-def compare(kind, z64, bias, p, got, index, chunk=8):
+def compare(kind, z64, bias, p, got, index, chunk=8, progress=None):
     """Errors of got (float32/float64 numpy, the GPU output) against the oracle.
 
     kind "start" / "rows": got[i] for every row i in ``index`` of z64 (rows of Z
     with the given bias [H][I][I]); kind "end": got[:, j] for every column j in
     ``index``.  Returns (max abs, relative L1, non-finite count, elements).
+    progress(done, total) is called as parts finish (long comparisons report
+    through it).
     """
     index = list(index)
     tasks = [(kind, index[k:k + chunk]) for k in range(0, len(index), chunk)]
     _G.update(z64=z64, bias=bias, p=p, got=got)
+    parts = []
     try:
         with mp.get_context("fork").Pool(min(workers(), len(tasks)), initializer=_limit_blas) as pool:
-            parts = pool.map(_part, tasks, chunksize=1)
+            for part in pool.imap_unordered(_part, tasks, chunksize=1):
+                parts.append(part)
+                if progress is not None:
+                    progress(len(parts), len(tasks))
     finally:
         _G.clear()
     esum = sum(x[0] for x in parts)

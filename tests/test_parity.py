@@ -7,8 +7,11 @@ Tolerances (compared element by element on the stored outputs, upcast exactly):
 Small and ragged sizes are compared on every output, and so is the I = 1024
 workload (both variants, over a process pool).  The I = 2048 and the row-block
 I = 4096 workloads are compared on ten and eight whole lines (every query block),
-with every output checked to be written and finite.
+with every output checked to be written and finite; with TRIATTN_FULL_PARITY=1
+they are also compared on every output.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -426,6 +429,83 @@ def test_workload_rows_4096():
     got = out[LINES_R1024].float().cpu().numpy()
     z64 = inputs.to_f64(torch.cat(host_rows)[LINES_R1024])
     _check_pool("rows", z64, bias64, p, got, range(len(LINES_R1024)), len(LINES_R1024) * I * 128, name)
+
+
+# Every output of the I = 2048 and I = 4096 row-block workloads: the oracle takes about
+# 7 and 13 minutes of host time on 16 cores, so these run only when asked for
+# (TRIATTN_FULL_PARITY=1); the line tests above cover every query block of both.
+FULL_PARITY = os.environ.get("TRIATTN_FULL_PARITY") == "1"
+full_only = pytest.mark.skipif(not FULL_PARITY, reason="every output of a large workload takes 7-13 min of "
+                               "host time for the oracle: set TRIATTN_FULL_PARITY=1")
+
+
+def _progress(what):
+    step = {"n": 0}
+
+    def report(done, total):
+        if done * 20 >= (step["n"] + 1) * total or done == total:
+            step["n"] = done * 20 // total
+            say(f"    {what}: oracle {done}/{total} parts")
+    return report
+
+
+@full_only
+@pytest.mark.timeout(1500)
+def test_workload_i2048_outliers_every_token():
+    """I = 2048 with outlier channels: all 2048 x 2048 x 128 outputs against the oracle."""
+    name = "start-bf16-I2048-outliers"
+    say(f"[workload] {name}: every token")
+    wl, w = _workload(name)
+    I = wl.I
+    z = inputs.workload_z(wl)
+    out = _nan_out((I, I, 128))
+    ta.triangle_attn_start(z.cuda(), dev(w), out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    del out
+    p = params64(w)
+    z64 = inputs.to_f64(z)
+    bias = ref.pair_bias(z64, p)
+    maxabs, rel, nonfin, n = oracle_pool.compare("start", z64, bias, p, got, range(I), chunk=4,
+                                                 progress=_progress(name))
+    say(f"    {name}: {n} outputs, max abs {maxabs:.3e}, rel L1 {rel:.3e}, non-finite {nonfin}")
+    assert n == I * I * 128 and nonfin == 0
+    assert maxabs <= BF16_MAX_ABS and rel <= BF16_REL_L1, f"{name}: max abs {maxabs:.3e}, rel L1 {rel:.3e}"
+
+
+@full_only
+@pytest.mark.timeout(1500)
+def test_workload_rows_4096_every_token():
+    """Row block of 1024 rows of I = 4096: all 1024 x 4096 x 128 outputs against the oracle."""
+    name = "rows-bf16-R1024-I4096"
+    say(f"[workload] {name}: every token")
+    wl, w = _workload(name)
+    I, R = wl.I, wl.n_rows
+    wd = dev(w)
+    p = params64(w)
+    bias = torch.empty((4, I, I), dtype=torch.float32, device="cuda")
+    bias64 = np.empty((4, I, I))
+    host_rows, dev_rows = [], []
+    for r0 in range(0, I, 512):
+        zb = inputs.workload_z(wl, r0, 512)
+        zbd = zb.cuda()
+        ta.triangle_attn_pair_bias(zbd, wd, row0=r0, bias=bias)
+        bias64[:, r0:r0 + 512] = ref.pair_bias(inputs.to_f64(zb), p)
+        if r0 < R:
+            host_rows.append(zb)
+            dev_rows.append(zbd)
+        say(f"  bias rows {r0}..{r0 + 511} done")
+    out = _nan_out((R, I, 128))
+    ta.triangle_attn_start_rows(torch.cat(dev_rows), bias, wd, out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    del out, bias, dev_rows
+    z64 = inputs.to_f64(torch.cat(host_rows))
+    maxabs, rel, nonfin, n = oracle_pool.compare("rows", z64, bias64, p, got, range(R), chunk=2,
+                                                 progress=_progress(name))
+    say(f"    {name}: {n} outputs, max abs {maxabs:.3e}, rel L1 {rel:.3e}, non-finite {nonfin}")
+    assert n == R * I * 128 and nonfin == 0
+    assert maxabs <= BF16_MAX_ABS and rel <= BF16_REL_L1, f"{name}: max abs {maxabs:.3e}, rel L1 {rel:.3e}"
 
 
 def test_small_bf16_i48_seed11():
