@@ -34,8 +34,10 @@
  *  - Every argument is validated on the host before anything is enqueued; on
  *    error nothing is launched and no output is touched.  Execution errors of
  *    an enqueued kernel surface at the caller's next synchronisation.
- *  - No global mutable state: calls are thread-safe; calls that share a
- *    workspace must be ordered by the caller (same stream or events).
+ *  - Calls are thread-safe; calls that share a workspace must be ordered by the
+ *    caller (same stream or events).  The only global state is a cache of each
+ *    device's CU count and, for triangle_attn_start_noalloc, a static device
+ *    array per GPU (calls of that entry point that overlap on one GPU race).
  *  - Supported shapes: c_z = 128, heads * head_dim = 128, head_dim = 32, any
  *    1 <= I <= 65536 (ragged tails handled), 1 <= rows <= I.
  */

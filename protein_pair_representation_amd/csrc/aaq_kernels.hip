@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "aaq_kernels.h"
 
 namespace aaq {
@@ -464,16 +466,18 @@ AAQ_KERNELS(B, 1, f32, float)
 AAQ_KERNELS(C, 2, f32, float)
 #undef AAQ_KERNELS
 
+// CUs of the current device, cached per device; concurrent first calls may both
+// query the device and store the same value (relaxed atomics, no data race).
 int cu_count() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int c = 0;
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-    cus[dev] = c;
+    cus[dev].store(c, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return c;
 }
 
 dim3 grid_for(int64_t n) {

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "triattn_kernels.h"
@@ -1683,14 +1684,16 @@ __global__ void __launch_bounds__(NTHREADS) tri_pack_bias(const float* __restric
 }
 
 // ---------------------------------------------------------------- launchers
+// CUs of the current device, cached per device; concurrent first calls may both
+// query the device and store the same value (relaxed atomics, no data race).
 static int cu_count() {
-  static int n = 0;
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
   if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    n = v;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
   return n;
 }
