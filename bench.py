@@ -576,6 +576,46 @@ def summarize_trace(run_dir, workload, steps, warmup, family="tri"):
     print("\n".join(out))
 
 
+ISSUE_PROBE_MODES = [  # (mode of csrc/issue_probe.hip, what one loop iteration issues, instructions per iteration)
+    (0, "v_exp_f32, 8 independent", 8),
+    (1, "v_exp_f16, 8 independent", 8),
+    (2, "v_cvt_pk_bf16_f32, 8 chained", 8),
+    (3, "v_mfma_f32_32x32x16_bf16, 4 independent", 4),
+    (4, "v_mfma_f32_16x16x32_bf16, 4 independent", 4),
+    (5, "phase: 4 + 2 products (in dependent pairs) alone", 6),
+    (6, "phase: 16 exp + 8 P conversions + 9 widenings alone", 33),
+    (7, "phase: both, one product per 5-6 VALU instructions", 39),
+]
+
+
+def issue_probe():
+    """Issue costs of the attention loop's instructions on this GPU (no memory traffic in the
+    measured loops), at two and three waves per SIMD; summary to profiles/issue_probe_gfx950.txt."""
+    import ctypes
+    from protein_pair_representation_amd.build import PROBE_PATH
+    if not os.path.exists(PROBE_PATH):
+        raise SystemExit(f"{PROBE_PATH} is missing: build it (python -m protein_pair_representation_amd.build)")
+    lib = ctypes.CDLL(PROBE_PATH)
+    lib.issue_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_double)]
+    lib.issue_probe_run.restype = ctypes.c_int
+    src = os.path.join(ROOT, "protein_pair_representation_amd", "csrc", "issue_probe.hip")
+    lines = ["# issue costs of the attention loop's instruction mix, gfx950 (MI355X); no memory traffic in the loops",
+             "# command: python3 bench.py --issue-probe",
+             f"# probe source sha={kernel_sha(src)}",
+             "# SIMD-cycles per loop iteration = kernel time x core clock / (waves per SIMD x iterations)",
+             f"{'loop body':54s} {'waves/SIMD':>10s} {'cyc/iter':>9s} {'cyc/instr':>9s} {'GHz':>5s}"]
+    for mode, what, ninstr in ISSUE_PROBE_MODES:
+        for w in (2, 3):
+            cyc, ghz = ctypes.c_double(), ctypes.c_double()
+            rc = lib.issue_probe_run(mode, w, ctypes.byref(cyc), ctypes.byref(ghz))
+            if rc != 0:
+                raise SystemExit(f"issue_probe_run({mode}, {w}) returned {rc}")
+            lines.append(f"{what:54s} {w:10d} {cyc.value:9.1f} {cyc.value / ninstr:9.2f} {ghz.value:5.2f}")
+    open(os.path.join(PROFILE_DIR, "issue_probe_gfx950.txt"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -603,6 +643,9 @@ def main():
     ap.add_argument("--summarize-sq", metavar="DIR",
                     help="write the attention kernel's SQ counter summary under profiles/ from rocprofv3 --pmc runs "
                          "in DIR, and exit")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="measure the issue costs of the attention loop's instruction mix (libissueprobe.so), "
+                         "write the summary under profiles/, and exit")
     ap.add_argument("--family", default="tri", choices=["tri", "aaq", "knn"],
                     help="kernel family of --summarize-pmc / --summarize-trace / --summarize-sq")
     args = ap.parse_args()
@@ -623,6 +666,10 @@ def main():
     import torch
     from protein_pair_representation_amd import inputs
     from protein_pair_representation_amd import triattn as ta
+
+    if args.issue_probe:
+        issue_probe()
+        return
 
     if args.copy_calibration:
         n = args.copy_calibration << 20

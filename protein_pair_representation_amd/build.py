@@ -18,6 +18,9 @@ SOURCES = [os.path.join(PKG_DIR, "csrc", "triattn_kernels.hip"),
            os.path.join(PKG_DIR, "csrc", "aaq_abi.cpp"),
            os.path.join(PKG_DIR, "csrc", "knn_kernels.hip"),
            os.path.join(PKG_DIR, "csrc", "knn_abi.cpp")]
+# measurement-only library: issue costs of the attention loop's instruction mix (bench.py --issue-probe)
+PROBE_PATH = os.path.join(PKG_DIR, "libissueprobe.so")
+PROBE_SOURCES = [os.path.join(PKG_DIR, "csrc", "issue_probe.hip")]
 ARCH = "gfx950"
 # Packed fp32 instructions are switched off for all device code.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -31,11 +34,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: cannot build libtriattn.so")
 
 
-def build(verbose: bool = False, out: str = LIB_PATH, extra_flags=()) -> str:
+def build(verbose: bool = False, out: str = LIB_PATH, extra_flags=(), sources=None) -> str:
     """Compile the kernels and the C ABI into `out` (always recompiles); extra_flags
     are added to the hipcc line (e.g. host-only instrumentation for a test build)."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-shared", "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
+    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-shared", "-I", os.path.join(ROOT, "include"),
+           *(sources or SOURCES), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,5 +53,11 @@ def build(verbose: bool = False, out: str = LIB_PATH, extra_flags=()) -> str:
     return out
 
 
+def build_probe(verbose: bool = False) -> str:
+    """Compile the issue-cost probe library (measurement only, not the attention path)."""
+    return build(verbose=verbose, out=PROBE_PATH, sources=PROBE_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))

@@ -5,6 +5,7 @@ Pointers here are fake device addresses: every case fails validation, which
 never dereferences a pointer and makes no HIP call, so this runs without a GPU.
 """
 import ctypes
+import os
 
 import pytest
 import torch
@@ -386,3 +387,20 @@ def test_knn_rejects(lib):
     assert call(nbr=A) == -7                                 # nbr overlaps x
     assert call(ws=A + 10 * MB + 1024) == -7                 # ws overlaps pair
     assert call(pair=A + 1 * MB) == -7                       # pair overlaps s
+
+
+def test_issue_probe_library_exports():
+    """The measurement-only probe library (bench.py --issue-probe) loads, exports its
+    two functions, and rejects bad arguments before any GPU call."""
+    import ctypes
+    from protein_pair_representation_amd.build import PROBE_PATH
+    if not os.path.exists(PROBE_PATH):
+        pytest.skip("libissueprobe.so not built")
+    lib = ctypes.CDLL(PROBE_PATH)
+    assert lib.issue_probe_modes() == 8
+    lib.issue_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_double)]
+    c, g = ctypes.c_double(), ctypes.c_double()
+    for mode, waves in ((-1, 2), (8, 2), (0, 0), (0, 5)):
+        assert lib.issue_probe_run(mode, waves, ctypes.byref(c), ctypes.byref(g)) == -1
+    assert lib.issue_probe_run(0, 2, None, ctypes.byref(g)) == -1
