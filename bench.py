@@ -727,7 +727,7 @@ def main():
     del z, wd, ws
     torch.cuda.empty_cache()
     if args.other_workloads:
-        # the other workloads of the survey, each measured the same way (fewer steps)
+        # the other workloads (I = 64 fp32, I = 384, I = 2048 with outliers, the I = 4096 row block), each measured the same way (fewer steps)
         others = {}
         for name in inputs.WORKLOADS:
             if name == wl.name:
