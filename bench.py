@@ -291,7 +291,7 @@ def kv_blocks(ws, wd, I, R, dt, variant, nb, stream, k2_flops, k2_ms, reps=10):
         vb = torch.zeros(v["vt"].shape[:3] + (npos,), dtype=dt, device="cuda")
         kb[:, :, :nk] = v["k"][:, :, k0:k0 + nk]
         vb[:, :, :, :nk] = v["vt"][:, :, :, k0:k0 + nk]
-        blocks.append((kb, vb, v["bias_f32"][:, :, k0:k0 + nk].contiguous(), nk))
+        blocks.append((kb, vb, v["bias_f32"][:, :, k0:k0 + nk].clone(), nk))   # a copy even for one block
     st = ta.state(I, R, dt, variant)
     out = torch.empty((R, I, 128), dtype=dt, device="cuda")
 
